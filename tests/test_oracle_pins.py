@@ -1,0 +1,340 @@
+"""Pins of the CPU oracle against things other than itself: the page's printed output,
+closed forms, brute force on tiny inputs, and library routines on special cases."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_inputs
+from synth.gen import accuracy_table
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LN3, LN7 = math.log(3.0), math.log(7.0)
+# exact SiLU values: sigma(ln 3) = 3/4, sigma(-ln 3) = 1/4, sigma(ln 7) = 7/8
+SILU_CLOSED = {0.0: 0.0, LN3: 0.75 * LN3, -LN3: -0.25 * LN3, LN7: 0.875 * LN7, -LN7: -0.125 * LN7}
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+# ------------------------------------------------------------------ heads
+
+def test_zero_init_matches_printed_example():
+    """Page example: zero-initialised FF layer + projection copied from lm_head makes every
+    head reproduce lm_head exactly; the page prints [True, True, True]."""
+    g = json.load(open(os.path.join(GOLDEN, "page_zero_init_example.json")))
+    inp = make_inputs("tiny", 0, zero_init=True)
+    assert (inp.cfg.H, inp.cfg.V, inp.cfg.K) == (g["hidden_size"], g["vocab_size"], g["num_heads"])
+    logits, ids, _, _ = oracle.heads_forward(inp.h, inp.w1, inp.b1, inp.w2, inp.cfg.s, "f32")
+    lm = oracle.lm_head_logits(inp.w_lm, oracle.as_f64(inp.h, "f32"), "f32")
+    printed = [bool(np.array_equal(logits[0, k], lm[0])) for k in range(inp.cfg.K)]
+    assert printed == g["printed"]
+    for k in range(inp.cfg.K):
+        np.testing.assert_array_equal(ids[0, k, : inp.cfg.s[k]], oracle.topk(lm[0], inp.cfg.s[k]))
+
+
+def test_zero_init_bf16_bitwise():
+    inp = make_inputs("small", 1, zero_init=True)
+    logits, _, _, u = oracle.heads_forward(inp.h, inp.w1, inp.b1, inp.w2, inp.cfg.s, "bf16")
+    lm = oracle.lm_head_logits(inp.w_lm, oracle.as_f64(inp.h, "bf16"), "bf16")
+    for k in range(inp.cfg.K):
+        assert np.array_equal(logits[0, k], lm[0])
+        assert np.array_equal(u[0, k], oracle.as_f64(inp.h, "bf16")[0])
+
+
+def test_heads_bias_silu_closed_form():
+    """W1 = 0, b1 with entries whose SiLU is known exactly, W2 = identity:
+    logits = h + SiLU(b1) (fp32 rounding of the stored bias aside)."""
+    H = 32
+    vals = list(SILU_CLOSED)
+    b1 = f32([[vals[i % 5] for i in range(H)]])
+    h = f32(np.linspace(-1, 1, H))[None, :]
+    w1 = np.zeros((1, H, H), np.float32)
+    w2 = np.eye(H, dtype=np.float32)[None]
+    logits, ids, _, u = oracle.heads_forward(h, w1, b1, w2, [3], "f32")
+    want = h[0].astype(np.float64) + np.array([SILU_CLOSED[vals[i % 5]] for i in range(H)])
+    np.testing.assert_allclose(logits[0, 0], want, rtol=1e-6, atol=1e-6)
+
+
+def test_heads_w1_orientation_and_residual():
+    """W1 = permutation matrix P (P[i, p(i)] = 1): z_i = h_{p(i)}, so u_i = h_i + SiLU(h_{p(i)}).
+    A transposed W1 would use p^-1; a dropped residual would lose h_i."""
+    H = 40
+    rng = np.random.default_rng(3)
+    keys = list(SILU_CLOSED)
+    h = f32([keys[i] for i in rng.integers(0, 5, size=H)])[None, :]
+    perm = rng.permutation(H)
+    assert not np.array_equal(perm, np.argsort(perm))
+    w1 = np.zeros((1, H, H), np.float32)
+    w1[0, np.arange(H), perm] = 1.0
+    b1 = np.zeros((1, H), np.float32)
+    V = 7
+    sel = rng.integers(0, H, size=V)
+    w2 = np.zeros((1, V, H), np.float32)
+    w2[0, np.arange(V), sel] = 1.0                  # logits_v = u[sel_v]
+    logits, _, _, u = oracle.heads_forward(h, w1, b1, w2, [2], "f32")
+    hd = h[0].astype(np.float64)
+    u_want = np.array([hd[i] + SILU_CLOSED[float(h[0, perm[i]])] if float(h[0, perm[i]]) in SILU_CLOSED
+                       else np.nan for i in range(H)])
+    # h values are float32 roundings of the keys; match them back to their exact key
+    u_want = np.array([hd[i] + SILU_CLOSED[min(keys, key=lambda k: abs(k - float(h[0, perm[i]])))]
+                       for i in range(H)])
+    np.testing.assert_allclose(u[0, 0], u_want, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(logits[0, 0], u_want[sel], rtol=1e-6, atol=1e-6)
+
+
+def test_silu_closed_forms_and_library():
+    import torch
+    for x, y in SILU_CLOSED.items():
+        assert oracle.silu(np.array([x]))[0] == pytest.approx(y, rel=1e-15, abs=1e-300)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    big = np.array([50.0, -50.0, 800.0, -800.0])
+    got = oracle.silu(big)
+    assert got[0] == pytest.approx(50.0, rel=1e-15) and abs(got[1]) < 1e-19
+    assert got[2] == 800.0 and got[3] == 0.0
+    x = np.random.default_rng(0).normal(0, 4, 1000)
+    lib = torch.nn.functional.silu(torch.tensor(x, dtype=torch.float64)).numpy()
+    np.testing.assert_allclose(oracle.silu(x), lib, rtol=1e-14, atol=1e-300)
+
+
+# ------------------------------------------------------------------ selection
+
+def test_topk_against_sorted_with_ties():
+    rng = np.random.default_rng(1)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        v = rng.integers(-3, 4, size=n).astype(np.float64)   # many ties
+        k = int(rng.integers(1, n + 1))
+        want = sorted(range(n), key=lambda i: (-v[i], i))[:k]
+        assert list(oracle.topk(v, k)) == want
+
+
+def test_argmax_lowest_against_loop():
+    rng = np.random.default_rng(2)
+    for _ in range(200):
+        v = rng.integers(-2, 3, size=int(rng.integers(1, 30))).astype(np.float64)
+        best = 0
+        for i in range(len(v)):
+            if v[i] > v[best]:
+                best = i
+        assert oracle.argmax_lowest(v) == best
+
+
+# ------------------------------------------------------------------ rounding
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    import torch
+    x = np.random.default_rng(4).normal(0, 3, 20000).astype(np.float32)
+    x = np.concatenate([x, np.float32([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0])])
+    want = torch.tensor(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_act(x.astype(np.float64), "bf16"), want)
+
+
+def test_round_bf16_brute_force_fp64():
+    """Nearest bf16 value with ties to even, found by scanning neighbouring bf16 values."""
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 1, 3000) * np.exp2(rng.integers(-20, 20, 3000))
+    x = np.concatenate([x, [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 2.0 - 2 ** -9]])
+    got = oracle.round_act(x, "bf16")
+    for xi, gi in zip(x, got):
+        b = int(np.float32(xi).view(np.uint32) >> 16)
+        cands = []
+        for c in range(b - 2, b + 3):
+            val = float(np.uint32((c & 0xFFFF) << 16).view(np.float32))
+            cands.append((abs(val - xi), c & 1, val))
+        best = min(cands)
+        assert gi == best[2], (xi, gi, best)
+    assert oracle.round_act(np.array([1.0 + 2 ** -8]), "bf16")[0] == 1.0
+    assert oracle.round_act(np.array([1.0 + 3 * 2 ** -8]), "bf16")[0] == 1.0 + 2 ** -6
+
+
+# ------------------------------------------------------------------ tree fill
+
+def test_build_tree_page_example():
+    g = json.load(open(os.path.join(GOLDEN, "page_tree_example.json")))
+    plan = oracle.plan_full(g["top_k"])
+    assert len(plan.leaves()) == g["candidates"]
+    topk = np.array([[[11, 12, -1], [21, 22, 23]]])
+    tokens, pos = oracle.build_tree(plan, np.array([7]), topk, np.array([5]))
+    assert tokens[0].tolist() == [7, 11, 12, 21, 22, 23, 21, 22, 23]
+    assert pos[0].tolist() == [5, 6, 6, 7, 7, 7, 7, 7, 7]
+
+
+# ------------------------------------------------------------------ tree attention
+
+def _brute_branch_attention(plan, q, kt, vt, kc, vc, L, scale):
+    """Each node's branch run on its own as a causal sequence [prefix; root..node]: the
+    newest token's attention over every row, with an explicit loop."""
+    B, N, Hq, d = q.shape
+    Hkv = kt.shape[2]
+    G = Hq // Hkv
+    out = np.zeros_like(q)
+    for b in range(B):
+        for i in range(N):
+            path = plan.path_nodes(i)
+            for j in range(Hq):
+                g = j // G
+                keys = [kc[b, t, g] for t in range(L[b])] + [kt[b, m, g] for m in path]
+                vals = [vc[b, t, g] for t in range(L[b])] + [vt[b, m, g] for m in path]
+                s = [float(np.dot(q[b, i, j], kk)) * scale for kk in keys]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                tot = sum(w)
+                acc = np.zeros(d)
+                for wi, vv in zip(w, vals):
+                    acc += wi * vv
+                out[b, i, j] = acc / tot
+    return out
+
+
+def _rand_attn(rng, B, N, Hq, Hkv, d, Lcap):
+    q = rng.normal(size=(B, N, Hq, d))
+    kt = rng.normal(size=(B, N, Hkv, d))
+    vt = rng.normal(size=(B, N, Hkv, d))
+    kc = rng.normal(size=(B, Lcap, Hkv, d)).astype(np.float32)
+    vc = rng.normal(size=(B, Lcap, Hkv, d)).astype(np.float32)
+    return q, kt, vt, kc, vc
+
+
+@pytest.mark.parametrize("tree_s,L", [((2, 3), 0), ((2, 3), 1), ((3, 2, 2), 7), ((1, 1, 1), 32),
+                                      ((4,), 5)])
+def test_tree_attention_equals_branches(tree_s, L):
+    rng = np.random.default_rng(len(tree_s) * 100 + L)
+    plan = oracle.plan_full(tree_s)
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    q, kt, vt, kc, vc = _rand_attn(rng, B, plan.n_nodes, Hq, Hkv, d, max(L, 1))
+    lens = np.array([L, max(L - 1, 0)])
+    got = oracle.tree_attention(plan, q, kt, vt, kc, vc, lens, "f32")
+    want = _brute_branch_attention(plan, q, kt, vt, kc.astype(np.float64), vc.astype(np.float64),
+                                   lens, 1 / math.sqrt(d))
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-7)
+
+
+def test_tree_attention_sparse_random_plans():
+    rng = np.random.default_rng(9)
+    for trial in range(6):
+        acc = np.sort(rng.uniform(0.05, 0.9, size=(3, 4)), axis=1)[:, ::-1]
+        plan = oracle.plan_from_accuracy(acc, (4, 3, 2), int(rng.integers(2, 17)))
+        q, kt, vt, kc, vc = _rand_attn(rng, 1, plan.n_nodes, 2, 1, 4, 9)
+        lens = np.array([int(rng.integers(0, 10))])
+        got = oracle.tree_attention(plan, q, kt, vt, kc, vc, lens, "f32")
+        want = _brute_branch_attention(plan, q, kt, vt, kc.astype(np.float64),
+                                       vc.astype(np.float64), lens, 0.5)
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-7)
+
+
+def test_chain_tree_is_causal_sdpa_with_gqa():
+    """All top-k = 1: the tree is one chain, so tree attention is ordinary causal attention
+    of the chain's tokens after the prefix (torch SDPA, float64, kv heads repeated)."""
+    import torch
+    rng = np.random.default_rng(11)
+    plan = oracle.plan_full((1, 1, 1, 1))
+    N, Hq, Hkv, d, L = plan.n_nodes, 6, 2, 16, 13
+    q, kt, vt, kc, vc = _rand_attn(rng, 1, N, Hq, Hkv, d, L)
+    got = oracle.tree_attention(plan, q, kt, vt, kc, vc, np.array([L]), "f32")
+    K = np.concatenate([kc[0].astype(np.float64), kt[0]], 0)     # [L+N, Hkv, d]
+    V = np.concatenate([vc[0].astype(np.float64), vt[0]], 0)
+    Qt = torch.tensor(q[0]).transpose(0, 1)[None]                # [1, Hq, N, d]
+    Kt = torch.tensor(K).transpose(0, 1).repeat_interleave(Hq // Hkv, 0)[None]
+    Vt = torch.tensor(V).transpose(0, 1).repeat_interleave(Hq // Hkv, 0)[None]
+    mask = torch.ones(N, L + N, dtype=torch.bool).tril(diagonal=L)
+    ref = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, attn_mask=mask)
+    want = ref[0].transpose(0, 1).numpy()
+    np.testing.assert_allclose(got[0], want, rtol=1e-6, atol=1e-7)
+
+
+def test_tree_attention_special_cases():
+    rng = np.random.default_rng(12)
+    plan = oracle.plan_full((2, 2))
+    q, kt, vt, kc, vc = _rand_attn(rng, 1, plan.n_nodes, 2, 2, 4, 4)
+    # empty prefix: the root sees only itself
+    got = oracle.tree_attention(plan, q, kt, vt, kc, vc, np.array([0]), "f32")
+    np.testing.assert_allclose(got[0, 0], oracle.round_act(vt[0, 0], "f32"), rtol=0, atol=0)
+    # equal keys everywhere: uniform weights, output is the mean of the visible values
+    kt[:] = 0.3
+    kc[:] = np.float32(0.3)
+    got = oracle.tree_attention(plan, q, kt, vt, kc, vc, np.array([4]), "f32")
+    for i in range(plan.n_nodes):
+        vis = np.concatenate([vc[0].astype(np.float64), vt[0, plan.path_nodes(i)]], 0)
+        np.testing.assert_allclose(got[0, i], vis.mean(0), rtol=1e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------------ verifier layer
+
+def test_proxy_qkv_and_out_selection_matrices():
+    rng = np.random.default_rng(13)
+    V, H, Hq, Hkv, d = 11, 8, 2, 1, 4
+    embed = rng.normal(size=(V, H)).astype(np.float32)
+    selq = rng.integers(0, H, size=Hq * d)
+    selk = rng.integers(0, H, size=Hkv * d)
+    wq = np.zeros((Hq * d, H), np.float32); wq[np.arange(Hq * d), selq] = 1
+    wk = np.zeros((Hkv * d, H), np.float32); wk[np.arange(Hkv * d), selk] = 2
+    wv = np.zeros((Hkv * d, H), np.float32); wv[np.arange(Hkv * d), selk] = -1
+    tokens = np.array([[3, 7, 0]])
+    x, q, k, v = oracle.proxy_qkv(tokens, embed, wq, wk, wv, Hq, Hkv, d, "f32")
+    e = embed[tokens[0]].astype(np.float64)
+    np.testing.assert_array_equal(x[0], e)
+    np.testing.assert_array_equal(q[0].reshape(3, -1), e[:, selq])          # head-major rows
+    np.testing.assert_array_equal(k[0].reshape(3, -1), 2 * e[:, selk])
+    np.testing.assert_array_equal(v[0].reshape(3, -1), -e[:, selk])
+    o = rng.normal(size=(1, 3, Hq, d)).astype(np.float32).astype(np.float64)
+    selo = rng.integers(0, Hq * d, size=H)
+    wo = np.zeros((H, Hq * d), np.float32); wo[np.arange(H), selo] = 1
+    nh = oracle.proxy_out(x, o, wo, "f32")
+    np.testing.assert_array_equal(nh[0], oracle.round_act(e + o[0].reshape(3, -1)[:, selo], "f32"))
+
+
+def test_verify_selection_matrix():
+    rng = np.random.default_rng(14)
+    V, H = 9, 6
+    sel = rng.integers(0, H, size=V)
+    c = rng.uniform(0.5, 2.0, size=V).astype(np.float32)
+    w = np.zeros((V, H), np.float32); w[np.arange(V), sel] = c
+    nh = rng.normal(size=(1, 4, H))
+    logits, am = oracle.verify(nh, w, "f32")
+    want = c.astype(np.float64)[None, :] * nh[0][:, sel]
+    np.testing.assert_allclose(logits[0], want, rtol=1e-15)
+    assert am[0].tolist() == [int(np.argmax(r)) for r in want]
+
+
+# ------------------------------------------------------------------ acceptance
+
+def test_accept_hand_cases():
+    plan = oracle.plan_full((2, 3))   # nodes: 0; (0,)=1 (1,)=2; (0,x)=3..5; (1,x)=6..8
+    tokens = np.array([[5, 10, 11, 20, 21, 22, 20, 21, 22]])
+    # root chooses 11 -> node 2; node 2 chooses 21 -> node 7; node 7 chooses 99
+    am = np.array([[11, 0, 21, 0, 0, 0, 0, 99, 0]])
+    a, nodes, toks = oracle.accept(plan, tokens, am)
+    assert a.tolist() == [2] and nodes[0].tolist() == [0, 2, 7] and toks[0].tolist() == [11, 21, 99]
+    # nothing accepted: only the root's own choice is emitted
+    am = np.array([[42, 20, 21, 0, 0, 0, 0, 0, 0]])
+    a, nodes, toks = oracle.accept(plan, tokens, am)
+    assert a.tolist() == [0] and nodes[0].tolist() == [0, -1, -1] and toks[0].tolist() == [42, -1, -1]
+    # a child would match, but its parent was rejected: depth stays 1
+    am = np.array([[10, 77, 20, 0, 0, 0, 0, 0, 0]])
+    a, nodes, toks = oracle.accept(plan, tokens, am)
+    assert a.tolist() == [1] and nodes[0].tolist() == [0, 1, -1] and toks[0].tolist() == [10, 77, -1]
+
+
+@pytest.mark.parametrize("cfg,seed", [("tiny", s) for s in range(6)] + [("small_batched", 0),
+                                                                         ("small", 1)])
+def test_step_equals_greedy_decoding(cfg, seed):
+    """Emitted tokens equal plain greedy decoding with the same verifier, and the accepted
+    length is maximal ("Medusa Decoding Heads", section "Diepe duik")."""
+    from tests import planting
+    inp = planting.planted_inputs(cfg, seed)
+    plan = planting.plan_for(inp.cfg, inp.acc)
+    res = oracle.step(inp, plan)
+    for b in range(inp.cfg.B):
+        a = int(res.accept_len[b])
+        g, _, _ = oracle.greedy_decode(inp, b, int(res.root[b]), a + 1)
+        assert res.accept_tokens[b, : a + 1].tolist() == g.tolist()
+        if a < plan.max_depth:
+            node = int(res.accept_nodes[b, a])
+            kids = [i for i in range(plan.n_nodes) if plan.parent[i] == node]
+            assert int(g[a]) not in {int(res.tokens[b, i]) for i in kids}
