@@ -1,0 +1,335 @@
+// Tree-masked attention (glossary "Medusa Heads", section "Attention arborescente et
+// acceptation"; codewithpapers abstract): every tree node attends to the cached prefix and
+// to the tree rows of its ancestors and itself, all nodes in one pass.
+//
+// Work split.  For one sequence b and one kv head g the query rows are the N*G
+// (node, query head) pairs of that group; they share every key, so they are the M side of
+// two MFMA contractions (scores and the value sum).  A workgroup takes 64 query rows (16
+// per wave) and one key range: a chunk of the prefix, or the tree keys.  Each 64-key
+// block is staged in LDS (K row-major, V transposed) and shared by the four waves.  Scores
+// are computed transposed, S^T = K Q^T, so each lane owns one query row; its softmax
+// state stays in registers and the value sum O^T = V^T P^T takes P^T straight from the
+// score registers (the two 16-key score tiles give each lane the eight key slots of one
+// 32-deep MFMA step; V^T is read from LDS with the same key order).  Partial (max, sum,
+// unnormalised output) per key range go to the workspace; a second kernel combines them.
+// The ancestor mask is one 64-bit word per (node, 64 keys).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace medusa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKeys = 64;          // keys staged per LDS block
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+    AttnShape s;
+    DevicePlan plan;
+    float scale_log2;
+    const void* q;
+    const void* k_tree;
+    const void* v_tree;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* prefix_lens;
+    void* out;
+    float* ws_o;    // [B][Hkv][slots][rows][d]
+    float* ws_ml;   // [B][Hkv][slots][rows][2]
+};
+
+template <typename T> struct Vt4;
+template <> struct Vt4<bf16_t> {
+    __device__ static __forceinline__ void load2(Frag<bf16_t>& f, const bf16_t* p0, const bf16_t* p1) {
+        const uint2 a = *reinterpret_cast<const uint2*>(p0);
+        const uint2 b = *reinterpret_cast<const uint2*>(p1);
+        f.v = u32x4{a.x, a.y, b.x, b.y};
+    }
+    __device__ static __forceinline__ void pack(Frag<bf16_t>& f, const float* p) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)f32_to_bf16(p[2 * i]) | ((uint32_t)f32_to_bf16(p[2 * i + 1]) << 16);
+        f.v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    __device__ static __forceinline__ bf16_t elem(const u32x4& v, int e) {
+        const uint32_t w = v[e >> 1];
+        return (bf16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+    }
+};
+template <> struct Vt4<float> {
+    __device__ static __forceinline__ void load2(Frag<float>& f, const float* p0, const float* p1) {
+        f.lo = *reinterpret_cast<const u32x4*>(p0);
+        f.hi = *reinterpret_cast<const u32x4*>(p1);
+    }
+    __device__ static __forceinline__ void pack(Frag<float>& f, const float* p) {
+        f.lo = u32x4{__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3])};
+        f.hi = u32x4{__float_as_uint(p[4]), __float_as_uint(p[5]), __float_as_uint(p[6]), __float_as_uint(p[7])};
+    }
+    __device__ static __forceinline__ float elem(const u32x4& v, int e) { return __uint_as_float(v[e]); }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a) {
+    constexpr int EPV = 16 / sizeof(T);
+    constexpr int KP = D + 8;          // K row pitch (elements)
+    constexpr int VP = kKeys + 8;      // V^T row pitch
+    constexpr int DS = D / 32;         // 32-deep steps over the head dim
+    constexpr int DT = D / 16;         // 16-wide output tiles over the head dim
+    __shared__ __align__(16) T Ks[kKeys * KP];
+    __shared__ __align__(16) T Vt[D * VP];
+
+    const AttnShape& sh = a.s;
+    const int n_slots = sh.n_splits + 1;
+    const int nblocks = sh.B * sh.Hkv * n_slots * sh.n_qblocks;
+    int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int qb = bid % sh.n_qblocks;
+    bid /= sh.n_qblocks;
+    const int slot = bid % n_slots;
+    bid /= n_slots;
+    const int g = bid % sh.Hkv;
+    const int b = bid / sh.Hkv;
+
+    const int L = min(max(a.prefix_lens[b], 0), sh.Lcap);
+    const bool tree = slot == sh.n_splits;
+    const int k_begin = tree ? 0 : slot * sh.chunk;
+    const int k_end = tree ? sh.N : min(L, k_begin + sh.chunk);
+    if (k_begin >= k_end) return;      // empty prefix chunk: the combine skips this slot
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int r = qb * 64 + wave * 16 + ln;          // this lane's query row
+    const bool row_ok = r < sh.rows;
+    const int node = row_ok ? r / sh.G : 0;
+    const int head = g * sh.G + (row_ok ? r % sh.G : 0);
+
+    const T* q = static_cast<const T*>(a.q) + (((long long)b * sh.N + node) * sh.Hq + head) * D;
+    Frag<T> qf[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+        if (row_ok) qf[ds].load(q + ds * 32 + 8 * lg);
+        else qf[ds].zero();
+    }
+
+    const T* ksrc;
+    const T* vsrc;
+    long long kstride;   // elements between consecutive keys
+    if (tree) {
+        ksrc = static_cast<const T*>(a.k_tree) + ((long long)b * sh.N * sh.Hkv + g) * D;
+        vsrc = static_cast<const T*>(a.v_tree) + ((long long)b * sh.N * sh.Hkv + g) * D;
+    } else {
+        ksrc = static_cast<const T*>(a.k_cache) + ((long long)b * sh.Lcap * sh.Hkv + g) * D;
+        vsrc = static_cast<const T*>(a.v_cache) + ((long long)b * sh.Lcap * sh.Hkv + g) * D;
+    }
+    kstride = (long long)sh.Hkv * D;
+
+    floatx4 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    for (int kb0 = k_begin; kb0 < k_end; kb0 += kKeys) {
+        __syncthreads();
+        constexpr int VPR = D / EPV;     // 16-byte vectors per key row
+        for (int idx = threadIdx.x; idx < kKeys * VPR; idx += kThreads) {
+            const int key = idx / VPR;
+            const int c = idx - key * VPR;
+            u32x4 kv = u32x4{0u, 0u, 0u, 0u};
+            u32x4 vv = kv;
+            if (kb0 + key < k_end) {
+                kv = *reinterpret_cast<const u32x4*>(ksrc + (long long)(kb0 + key) * kstride + c * EPV);
+                vv = *reinterpret_cast<const u32x4*>(vsrc + (long long)(kb0 + key) * kstride + c * EPV);
+            }
+            *reinterpret_cast<u32x4*>(Ks + key * KP + c * EPV) = kv;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) Vt[(c * EPV + e) * VP + key] = Vt4<T>::elem(vv, e);
+        }
+        __syncthreads();
+        uint64_t mword = ~0ull;
+        if (tree) mword = row_ok ? a.plan.mask[(long long)node * a.plan.mask_words + (kb0 >> 6)] : 0ull;
+
+#pragma unroll
+        for (int kb = 0; kb < kKeys; kb += 32) {
+            if (kb0 + kb >= k_end) break;
+            floatx4 sc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    Frag<T> kf;
+                    kf.load(Ks + (kb + t * 16 + ln) * KP + ds * 32 + 8 * lg);
+                    mma(sc[t], kf, qf[ds]);
+                }
+            }
+            // sc[t][j]: score of this lane's row against key kb0 + kb + 16 t + 4 lg + j
+            float p[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int kl = kb + t * 16 + 4 * lg + j;        // key within the block
+                    bool ok = row_ok && kb0 + kl < k_end;
+                    if (tree) ok = ok && ((mword >> kl) & 1ull);
+                    const float v = ok ? sc[t][j] * a.scale_log2 : -INFINITY;
+                    p[t * 4 + j] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, shfl_xor_f(mx, 16));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            float alpha = 1.f;
+            if (m_new == -INFINITY) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] = 0.f;
+            } else {
+                alpha = exp2f(m_run - m_new);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] = exp2f(p[e] - m_new);
+            }
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) psum += p[e];
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            Frag<T> pf;
+            Vt4<T>::pack(pf, p);
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                o[t] *= alpha;
+                Frag<T> vf;
+                const T* vrow = Vt + (t * 16 + ln) * VP + kb + 4 * lg;
+                Vt4<T>::load2(vf, vrow, vrow + 16);
+                mma(o[t], vf, pf);
+            }
+        }
+    }
+    l_run += shfl_xor_f(l_run, 16);
+    l_run += shfl_xor_f(l_run, 32);
+    if (!row_ok) return;
+    const long long base = ((((long long)b * sh.Hkv + g) * n_slots + slot) * sh.rows + r);
+    float* wo = a.ws_o + base * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+        *reinterpret_cast<floatx4*>(wo + t * 16 + 4 * lg) = o[t];
+    if (lg == 0) {
+        a.ws_ml[base * 2 + 0] = m_run;
+        a.ws_ml[base * 2 + 1] = l_run;
+    }
+}
+
+// One wave per (sequence, node, query head): combine the key ranges.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnArgs a) {
+    using E = Elem<T>;
+    constexpr int PER = D / kWave;
+    const AttnShape& sh = a.s;
+    const int row_id = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row_id >= sh.B * sh.N * sh.Hq) return;
+    const int j = row_id % sh.Hq;
+    const int i = (row_id / sh.Hq) % sh.N;
+    const int b = row_id / (sh.Hq * sh.N);
+    const int g = j / sh.G;
+    const int r = i * sh.G + (j - g * sh.G);
+    const int n_slots = sh.n_splits + 1;
+    const int L = min(max(a.prefix_lens[b], 0), sh.Lcap);
+
+    float mx = -INFINITY;
+    for (int s = 0; s < n_slots; ++s) {
+        if (s < sh.n_splits && s * sh.chunk >= L) continue;
+        const long long base = (((long long)b * sh.Hkv + g) * n_slots + s) * sh.rows + r;
+        mx = fmaxf(mx, a.ws_ml[base * 2]);
+    }
+    float den = 0.f;
+    float num[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] = 0.f;
+    for (int s = 0; s < n_slots; ++s) {
+        if (s < sh.n_splits && s * sh.chunk >= L) continue;
+        const long long base = (((long long)b * sh.Hkv + g) * n_slots + s) * sh.rows + r;
+        const float w = exp2f(a.ws_ml[base * 2] - mx);
+        den += w * a.ws_ml[base * 2 + 1];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] += w * a.ws_o[base * D + lane + kWave * e];
+    }
+    const float inv = 1.f / den;
+    T* out = static_cast<T*>(a.out) + (((long long)b * sh.N + i) * sh.Hq + j) * D;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[lane + kWave * e] = E::from_f32(num[e] * inv);
+}
+
+template <typename T, int D>
+hipError_t launch_td(const AttnArgs& a, hipStream_t stream) {
+    const AttnShape& s = a.s;
+    const int nblocks = s.B * s.Hkv * (s.n_splits + 1) * s.n_qblocks;
+    prof_begin("attn_partial", stream);
+    hipLaunchKernelGGL((attn_partial_kernel<T, D>), dim3(nblocks), dim3(kThreads), 0, stream, a);
+    prof_end(stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int rows = s.B * s.N * s.Hq;
+    prof_begin("attn_combine", stream);
+    hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((rows + 3) / 4), dim3(kThreads), 0, stream, a);
+    prof_end(stream);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+AttnShape attn_shape(int B, int N, int Hq, int Hkv, int d, int Lcap) {
+    AttnShape s{};
+    s.B = B; s.N = N; s.Hq = Hq; s.Hkv = Hkv; s.d = d; s.Lcap = Lcap;
+    s.G = Hq / Hkv;
+    s.rows = N * s.G;
+    s.n_qblocks = (s.rows + 63) / 64;
+    // Split the prefix so that (a) the partial outputs (rows * d fp32 per split) stay
+    // below about half the K/V bytes they summarise and (b) the grid still covers the
+    // chip when there are few (sequence, kv head, query block) triples.
+    const int max_splits = Lcap > 0 ? (Lcap + kKeys - 1) / kKeys : 1;
+    int splits = Lcap / (2 * s.rows);
+    const int base = B * Hkv * s.n_qblocks;
+    const int fill = (512 + base - 1) / base;
+    if (splits < fill) splits = fill;
+    if (splits < 1) splits = 1;
+    if (splits > max_splits) splits = max_splits;
+    int chunk = Lcap > 0 ? (Lcap + splits - 1) / splits : kKeys;
+    chunk = (chunk + kKeys - 1) / kKeys * kKeys;
+    s.chunk = chunk;
+    s.n_splits = Lcap > 0 ? (Lcap + chunk - 1) / chunk : 0;
+    return s;
+}
+
+size_t attn_workspace_bytes(const AttnShape& s) {
+    const size_t slots = (size_t)s.n_splits + 1;
+    const size_t rows = (size_t)s.B * s.Hkv * slots * s.rows;
+    return rows * (size_t)s.d * sizeof(float) + rows * 2 * sizeof(float) + 256;
+}
+
+hipError_t attention_launch(medusa_dtype dt, const AttnShape& s, const DevicePlan& plan, float scale,
+                            const void* q, const void* k_tree, const void* v_tree,
+                            const void* k_cache, const void* v_cache, const int32_t* prefix_lens,
+                            void* out, void* ws, hipStream_t stream) {
+    AttnArgs a;
+    a.s = s;
+    a.plan = plan;
+    a.scale_log2 = scale * kLog2e;
+    a.q = q; a.k_tree = k_tree; a.v_tree = v_tree; a.k_cache = k_cache; a.v_cache = v_cache;
+    a.prefix_lens = prefix_lens;
+    a.out = out;
+    const size_t slots = (size_t)s.n_splits + 1;
+    const size_t rows = (size_t)s.B * s.Hkv * slots * s.rows;
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_ml = a.ws_o + rows * s.d;
+    if (dt == MEDUSA_BF16) {
+        return s.d == 64 ? launch_td<bf16_t, 64>(a, stream) : launch_td<bf16_t, 128>(a, stream);
+    }
+    return s.d == 64 ? launch_td<float, 64>(a, stream) : launch_td<float, 128>(a, stream);
+}
+
+}  // namespace medusa

@@ -1,0 +1,120 @@
+// Internal interfaces between the C-ABI layer (api.cpp) and the kernels (*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/medusa.h"
+
+namespace medusa {
+
+// ------------------------------------------------------------------ skinny GEMM
+// Y[m, n] = sum_k X[m, k] * W[n, k] for up to kMaxProblems independent problems that
+// share M and K, in one launch.  W streams from HBM once; X rows are staged in LDS.
+constexpr int kMaxProblems = 9;
+
+enum Epilogue : int {
+    EPI_STORE = 0,   // out[m*ldo + n] = rnd(silu?(acc + bias[n]) + residual[m][n])
+    EPI_TOPS = 1,    // per row m: the tile's top-s (value desc, id asc) -> partials
+    EPI_ARGMAX = 2,  // per row m: the tile's best (value, id) -> partials
+};
+
+struct GemmProblem {
+    const void* W;            // [N, K]
+    const void* X;            // row m at X + (x_rows ? x_rows[m] : m) * x_stride
+    const int32_t* x_rows;    // optional row gather (ids outside [0, x_rows_bound) read zeros)
+    long long x_stride;       // elements
+    int N;
+    int tile_begin;           // first flattened tile of this problem
+    int n_tiles;
+    // EPI_STORE
+    void* out;                // element type T
+    long long ldo;
+    const void* bias;         // [N] T or null
+    int silu;                 // apply SiLU after the bias
+    const void* res;          // residual rows (T) or null
+    const int32_t* res_rows;  // optional residual gather
+    long long res_stride;
+    // EPI_TOPS / EPI_ARGMAX
+    int s;                    // candidates kept per tile (1 for EPI_ARGMAX)
+    float* logits;            // optional fp32 [M, N] with row stride logits_ld
+    long long logits_ld;
+    float* part_val;          // [M, n_tiles, s]
+    int32_t* part_idx;
+};
+
+struct GemmBatch {
+    GemmProblem p[kMaxProblems];
+    int n_problems;
+    int total_tiles;
+    int M;
+    int K;
+    int KC;                   // contraction chunk staged in LDS per pass
+    int x_rows_bound;
+    int res_rows_bound;
+};
+
+// Rows of W per workgroup for a given configuration.
+int gemm_rows_per_tile(medusa_dtype dt, int M, int epi);
+// Fills KC and launches.  Returns hipSuccess or the launch error.
+hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& batch, hipStream_t stream);
+
+// ------------------------------------------------------------------ top-s merge
+struct MergeProblem {
+    const float* part_val;    // [M, n_tiles, s]
+    const int32_t* part_idx;
+    int n_tiles;
+    int s;
+    int32_t* out_ids;         // row m at out_ids + m * out_ld ; s_pad entries written
+    float* out_vals;          // may be null
+    long long out_ld;
+    int s_pad;                // entries written per row (>= s); the rest get -1 / 0
+};
+struct MergeBatch {
+    MergeProblem p[kMaxProblems];
+    int n_problems;
+    int M;
+};
+hipError_t topk_merge_launch(const MergeBatch& batch, hipStream_t stream);
+
+// ------------------------------------------------------------------ tree
+struct DevicePlan {
+    const int32_t* parent;
+    const int32_t* depth;
+    const int32_t* rank;
+    const uint64_t* mask;
+    int n_nodes;
+    int max_depth;
+    int mask_words;
+};
+hipError_t build_tree_launch(const DevicePlan& plan, int B, int K, int s_max,
+                             const int32_t* root_ids, const int32_t* topk_ids,
+                             const int32_t* prefix_lens, int32_t* node_tokens,
+                             int32_t* position_ids, hipStream_t stream);
+hipError_t accept_launch(const DevicePlan& plan, int B, int n_tiles, const float* part_val,
+                         const int32_t* part_idx, const int32_t* node_tokens,
+                         int32_t* node_argmax, int32_t* accept_len, int32_t* accept_nodes,
+                         int32_t* accept_tokens, hipStream_t stream);
+
+// ------------------------------------------------------------------ attention
+struct AttnShape {
+    int B, N, Hq, Hkv, d, Lcap;
+    int G;          // Hq / Hkv
+    int rows;       // N * G query rows per (sequence, kv head)
+    int n_qblocks;  // ceil(rows / 64)
+    int chunk;      // prefix keys per split (multiple of 64)
+    int n_splits;   // prefix splits; one more slot holds the tree keys
+};
+AttnShape attn_shape(int B, int N, int Hq, int Hkv, int d, int Lcap);
+size_t attn_workspace_bytes(const AttnShape& s);
+hipError_t attention_launch(medusa_dtype dt, const AttnShape& s, const DevicePlan& plan, float scale,
+                            const void* q, const void* k_tree, const void* v_tree,
+                            const void* k_cache, const void* v_cache, const int32_t* prefix_lens,
+                            void* out, void* ws, hipStream_t stream);
+
+// ------------------------------------------------------------------ profiling
+void prof_begin(const char* name, hipStream_t stream);
+void prof_end(hipStream_t stream);
+
+}  // namespace medusa

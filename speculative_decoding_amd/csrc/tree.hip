@@ -1,0 +1,127 @@
+// Tree fill and greedy acceptance.
+//
+// Tree fill (glossary "Medusa Heads", section "Attention arborescente et acceptation"):
+// node 0 carries the root token, a depth-d node with rank r carries head d's rank-r
+// candidate; every head-d candidate appears under every depth-(d-1) node that the plan
+// keeps, which is why the plan (parent/depth/rank) is static and only the tokens change.
+//
+// Acceptance (same section): a candidate is accepted when it equals the model's first
+// choice at its parent; the longest accepted branch is kept and the deepest accepted
+// node's own first choice is emitted after it.
+#include "common.hpp"
+#include "internal.hpp"
+
+#include <limits.h>
+
+namespace medusa {
+
+namespace {
+
+__global__ __launch_bounds__(256) void build_tree_kernel(DevicePlan plan, int K, int s_max,
+                                                         const int32_t* __restrict__ root_ids,
+                                                         const int32_t* __restrict__ topk_ids,
+                                                         const int32_t* __restrict__ prefix_lens,
+                                                         int32_t* __restrict__ node_tokens,
+                                                         int32_t* __restrict__ position_ids) {
+    const int b = blockIdx.y;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int N = plan.n_nodes;
+    if (i >= N) return;
+    const int d = plan.depth[i];
+    const int tok = d == 0 ? root_ids[b]
+                           : topk_ids[((long long)b * K + (d - 1)) * s_max + plan.rank[i]];
+    node_tokens[(long long)b * N + i] = tok;
+    if (position_ids) position_ids[(long long)b * N + i] = (prefix_lens ? prefix_lens[b] : 0) + d;
+}
+
+constexpr int kAcceptThreads = 256;
+constexpr int kMaxNodes = MEDUSA_MAX_NODES;
+
+// One workgroup per sequence: merge the lm_head argmax partials of every node, then walk
+// the tree level by level.
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
+    DevicePlan plan, int n_tiles, const float* __restrict__ part_val,
+    const int32_t* __restrict__ part_idx, const int32_t* __restrict__ node_tokens,
+    int32_t* __restrict__ node_argmax, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ accept_nodes, int32_t* __restrict__ accept_tokens) {
+    __shared__ int s_arg[kMaxNodes];
+    __shared__ unsigned char s_acc[kMaxNodes];
+    __shared__ int s_best;
+    const int b = blockIdx.x;
+    const int N = plan.n_nodes;
+    const int D = plan.max_depth;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    constexpr int kWaves = kAcceptThreads / kWave;
+
+    for (int i = wave; i < N; i += kWaves) {
+        const long long base = ((long long)b * N + i) * n_tiles;
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        for (int t = lane; t < n_tiles; t += kWave) {
+            const float v = part_val[base + t];
+            const int id = part_idx[base + t];
+            if (better(v, id, bv, bi)) { bv = v; bi = id; }
+        }
+        reduce_best<kWave>(bv, bi);
+        if (lane == 0) {
+            s_arg[i] = bi;
+            if (node_argmax) node_argmax[(long long)b * N + i] = bi;
+        }
+    }
+    for (int i = threadIdx.x; i < N; i += kAcceptThreads) s_acc[i] = i == 0;
+    if (threadIdx.x == 0) s_best = 0;
+    __syncthreads();
+    const int32_t* tok = node_tokens + (long long)b * N;
+    for (int d = 1; d <= D; ++d) {
+        for (int i = threadIdx.x; i < N; i += kAcceptThreads) {
+            if (plan.depth[i] != d) continue;
+            const int p = plan.parent[i];
+            s_acc[i] = s_acc[p] && tok[i] == s_arg[p];
+        }
+        __syncthreads();
+    }
+    // deepest accepted node (unique: siblings carry distinct tokens); lowest index on ties
+    for (int i = threadIdx.x; i < N; i += kAcceptThreads)
+        if (s_acc[i]) atomicMax(&s_best, (plan.depth[i] << 16) | (0xFFFF - i));
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int best = 0xFFFF - (s_best & 0xFFFF);
+        const int a = plan.depth[best];
+        accept_len[b] = a;
+        int32_t* an = accept_nodes + (long long)b * (D + 1);
+        int32_t* at = accept_tokens + (long long)b * (D + 1);
+        for (int j = a + 1; j <= D; ++j) { an[j] = -1; at[j] = -1; }
+        int node = best;
+        for (int j = a; j >= 0; --j) {
+            an[j] = node;
+            if (j >= 1) at[j - 1] = tok[node];
+            node = plan.parent[node];
+        }
+        at[a] = s_arg[best];
+    }
+}
+
+}  // namespace
+
+hipError_t build_tree_launch(const DevicePlan& plan, int B, int K, int s_max,
+                             const int32_t* root_ids, const int32_t* topk_ids,
+                             const int32_t* prefix_lens, int32_t* node_tokens,
+                             int32_t* position_ids, hipStream_t stream) {
+    dim3 grid((plan.n_nodes + 255) / 256, B);
+    hipLaunchKernelGGL(build_tree_kernel, grid, dim3(256), 0, stream, plan, K, s_max, root_ids,
+                       topk_ids, prefix_lens, node_tokens, position_ids);
+    return hipGetLastError();
+}
+
+hipError_t accept_launch(const DevicePlan& plan, int B, int n_tiles, const float* part_val,
+                         const int32_t* part_idx, const int32_t* node_tokens,
+                         int32_t* node_argmax, int32_t* accept_len, int32_t* accept_nodes,
+                         int32_t* accept_tokens, hipStream_t stream) {
+    hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(kAcceptThreads), 0, stream, plan, n_tiles,
+                       part_val, part_idx, node_tokens, node_argmax, accept_len, accept_nodes,
+                       accept_tokens);
+    return hipGetLastError();
+}
+
+}  // namespace medusa

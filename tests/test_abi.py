@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, builds the
+same tree plans as the oracle, and rejects bad arguments before touching a device."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import CONFIGS, make_inputs
+from synth.gen import accuracy_table
+
+M = pytest.importorskip("speculative_decoding_amd.medusa")
+from speculative_decoding_amd import header_functions, lib  # noqa: E402
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def test_exports_every_header_symbol():
+    L = lib()
+    names = header_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), f"libmedusa.so does not export {n}"
+
+
+def _same_plan(cplan, oplan):
+    parent, depth, rank, mask = cplan.arrays()
+    np.testing.assert_array_equal(parent, oplan.parent)
+    np.testing.assert_array_equal(depth, oplan.depth)
+    np.testing.assert_array_equal(rank, oplan.rank)
+    np.testing.assert_array_equal(mask, oplan.mask_bits())
+    assert cplan.info() == (oplan.n_nodes, oplan.max_depth, oplan.mask_words)
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_plan_matches_oracle(name):
+    cfg = CONFIGS[name]
+    if cfg.tree == "full":
+        _same_plan(M.medusa_tree_plan_full(cfg.tree_s), oracle.plan_full(cfg.tree_s))
+    else:
+        for seed in range(3):
+            acc = accuracy_table(cfg, seed)
+            _same_plan(M.medusa_tree_plan_from_accuracy(acc, cfg.tree_s, cfg.n_nodes),
+                       oracle.plan_from_accuracy(acc, cfg.tree_s, cfg.n_nodes))
+
+
+def test_plan_from_paths_matches_oracle():
+    paths = [(1,), (0,), (0, 2), (0, 0), (1, 0), (0, 0, 3)]
+    _same_plan(M.medusa_tree_plan_create(paths), oracle.plan_from_paths(paths))
+    _same_plan(M.medusa_tree_plan_create([]), oracle.plan_from_paths([]))
+
+
+@pytest.mark.parametrize("paths", [[(0, 1)],             # parent (0,) missing
+                                   [(0,), (0,)],         # duplicate
+                                   [(0,), (64,)]])       # rank beyond the top-k limit
+def test_plan_rejects_malformed(paths):
+    with pytest.raises(M.MedusaError) as e:
+        M.medusa_tree_plan_create(paths)
+    assert e.value.status == 4
+
+
+def test_plan_rejects_rank_after_padding():
+    flat = np.array([[0, -1, 2]], np.int32)
+    out = ctypes.c_void_p()
+    st = lib().medusa_tree_plan_create(flat.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 1, 3,
+                                       ctypes.byref(out))
+    assert st == 4
+
+
+def test_plan_too_many_nodes():
+    with pytest.raises(M.MedusaError) as e:
+        M.medusa_tree_plan_full((64, 64))
+    assert e.value.status == 2
+
+
+# ------------------------------------------------------------------ error paths
+FAKE = 1 << 20      # aligned, never dereferenced: every call below fails before any launch
+
+
+def _heads(**over):
+    a = dict(dt=1, B=1, H=256, V=1000, K=3, hidden=FAKE, w1=FAKE, b1=FAKE, w2=FAKE, w_lm=None,
+             s=[2, 3, 3], s_max=3, topk_ids=FAKE, topk_vals=FAKE, root=None, u=None, logits=None,
+             ws=FAKE, ws_bytes=1 << 40)
+    a.update(over)
+    s = (ctypes.c_int32 * len(a["s"]))(*a["s"])
+    return lib().medusa_heads_forward(a["dt"], a["B"], a["H"], a["V"], a["K"], a["hidden"], a["w1"],
+                                      a["b1"], a["w2"], a["w_lm"], s, a["s_max"], a["topk_ids"],
+                                      a["topk_vals"], a["root"], a["u"], a["logits"], a["ws"],
+                                      a["ws_bytes"], None)
+
+
+def test_heads_error_paths():
+    assert _heads(hidden=None) == 1
+    assert _heads(w_lm=FAKE, root=None) == 1
+    assert _heads(dt=7) == 3
+    assert _heads(H=100) == 2
+    assert _heads(K=9) == 2
+    assert _heads(s=[2, 65, 3], s_max=65) == 3
+    assert _heads(s=[2, 3, 3], s_max=2) == 2
+    assert _heads(hidden=FAKE + 8) == 2                    # misaligned
+    assert _heads(ws=None) == 5
+    assert _heads(ws_bytes=16) == 5
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-device status; a GPU is visible")
+def test_no_device_status():
+    assert _heads() == 6
+
+
+def test_workspace_queries_positive():
+    assert M.medusa_heads_workspace("bf16", 1, 4096, 128256, 4, 10) > 0
+    plan = M.medusa_tree_plan_full((2, 3))
+    assert M.medusa_attention_workspace(plan, "bf16", 1, 32, 8, 128, 4096) > 0
+    assert M.medusa_verify_workspace(plan, "bf16", 1, 4096, 128256) > 0
+    assert M.medusa_attention_workspace(plan, "bf16", 1, 32, 8, 96, 4096) == 0   # d unsupported
+
+
+def test_tree_and_attention_error_paths():
+    plan = M.medusa_tree_plan_full((2, 3))
+    s = (ctypes.c_int32 * 3)(2, 3, 3)
+    L = lib()
+    # not uploaded
+    assert L.medusa_build_tree(plan.handle, 1, 3, 3, s, FAKE, FAKE, None, FAKE, None, None) == 8
+    # plan deeper than the heads
+    assert L.medusa_build_tree(plan.handle, 1, 1, 3, s, FAKE, FAKE, None, FAKE, None, None) == 4
+    # plan rank 2 at depth 1 is not < s[0] = 2
+    big = M.medusa_tree_plan_full((3, 3))
+    assert L.medusa_build_tree(big.handle, 1, 3, 3, s, FAKE, FAKE, None, FAKE, None, None) == 4
+    assert L.medusa_tree_attention(plan.handle, 1, 1, 32, 8, 96, 64, 0.0, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 3
+    assert L.medusa_tree_attention(plan.handle, 1, 1, 30, 8, 128, 64, 0.0, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 2
+    assert L.medusa_tree_attention(plan.handle, 1, 1, 32, 8, 128, 64, 0.0, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, 8, None) == 5
+    assert L.medusa_tree_attention(plan.handle, 1, 1, 32, 8, 128, 64, 0.0, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 8
+    assert L.medusa_verify_accept(plan.handle, 1, 1, 4096, 1000, FAKE, FAKE, FAKE, None, FAKE,
+                                  None, FAKE, None, FAKE, 1 << 40, None) == 1
+    assert L.medusa_verify_accept(plan.handle, 1, 1, 4095, 1000, FAKE, FAKE, FAKE, None, FAKE,
+                                  FAKE, FAKE, None, FAKE, 1 << 40, None) == 2
+    assert L.medusa_proxy_qkv(1, 9, 256, 1000, 4, 4, 64, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, None) == 1
+    assert L.medusa_proxy_out(1, 9, 250, 1000, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.medusa_status_string(5) == b"workspace too small"

@@ -1,0 +1,92 @@
+"""GPU parity: the HIP step through the C ABI against the CPU oracle, on seeded planted
+inputs whose every discrete decision has a margin >= 1e-2 (so ids and accept lengths
+must match bit for bit; floating outputs within 1e-3 + 2e-2 |oracle|)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import get_config, make_inputs
+from tests.gpu_util import (compare_step, close, exact, gpu_plan, oracle_plan, planted, run_gpu,
+                            say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from speculative_decoding_amd import lib
+    lib()   # fails loudly when libmedusa.so is missing
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("seed", list(range(20)))
+def test_tiny_step(dev, seed):
+    say(f"[tiny seed {seed}]")
+    inp = planted("tiny", seed)
+    ref = oracle.step(inp, oracle_plan(inp))
+    _, got = run_gpu(inp, dev)
+    compare_step(inp, got, ref)
+
+
+@pytest.mark.parametrize("cfg,seed", [("small", 0), ("small", 1), ("small", 2),
+                                      ("small_batched", 0), ("small_batched", 1)])
+def test_small_step(dev, cfg, seed):
+    say(f"[{cfg} seed {seed}]")
+    inp = planted(cfg, seed)
+    ref = oracle.step(inp, oracle_plan(inp))
+    _, got = run_gpu(inp, dev)
+    compare_step(inp, got, ref)
+
+
+def test_zero_init_heads_bitwise(dev):
+    """Zero-initialised FF layer and projections copied from lm_head: every head's logits
+    equal lm_head's bit for bit on the GPU (glossary "Medusa Heads", printed [True, True,
+    True] in section "Comment les têtes prédisent les tokens suivants")."""
+    for cfg in ("tiny", "small"):
+        say(f"[zero-init {cfg}]")
+        inp = make_inputs(cfg, 3, zero_init=True)
+        _, got = run_gpu(inp, dev)
+        hl = got["head_logits"]
+        for k in range(inp.cfg.K):
+            assert np.array_equal(hl[:, k].view(np.uint32), hl[:, inp.cfg.K].view(np.uint32)), \
+                f"{cfg}: head {k} logits differ from lm_head bitwise"
+            exact(f"{cfg} head {k} top-1 vs root", got["topk_ids"][:, k, 0], got["root_ids"])
+
+
+def test_run_twice_bitwise(dev):
+    """No atomics on values and fixed reduction orders: two runs give identical bits."""
+    say("[determinism small_batched 0]")
+    inp = planted("small_batched", 0)
+    step, a = run_gpu(inp, dev)
+    import torch
+    step.run(bootstrap_root=True)
+    torch.cuda.synchronize()
+    b = step.results()
+    for k, v in a.items():
+        if v is None:
+            continue
+        assert np.array_equal(v, b[k]), f"{k} differs between runs"
+
+
+def test_accepted_tokens_equal_greedy(dev):
+    """The step's emitted tokens are exactly the greedy continuation of the root
+    ("Medusa Decoding Heads", section "Diepe duik")."""
+    for cfg, seed in (("tiny", 1), ("small", 0), ("small_batched", 2)):
+        say(f"[greedy {cfg} seed {seed}]")
+        inp = planted(cfg, seed)
+        _, got = run_gpu(inp, dev, keep_logits=False)
+        plan = oracle_plan(inp)
+        for b in range(inp.cfg.B):
+            a = int(got["accept_len"][b])
+            g, _, _ = oracle.greedy_decode(inp, b, int(got["root_ids"][b]), a + 1)
+            exact(f"{cfg} b{b} emitted vs greedy", got["accept_tokens"][b, : a + 1], g)
+            if a < plan.max_depth:      # the next greedy token is not a child candidate
+                node = int(got["accept_nodes"][b, a])
+                kids = [i for i in range(plan.n_nodes) if plan.parent[i] == node]
+                toks = {int(got["node_tokens"][b, i]) for i in kids}
+                g2, _, _ = oracle.greedy_decode(inp, b, int(got["root_ids"][b]), a + 1)
+                assert int(g2[a]) not in toks
