@@ -1,0 +1,225 @@
+"""Benchmark: Medusa decode steps on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input: heads (residual SiLU
+block, vocabulary projections, per-head top-k) -> tree fill -> verifier Q/K/V ->
+tree-masked attention -> verifier output -> lm_head verification + acceptance.
+Inputs are resident in HBM before timing starts.  Prints one JSON line on stdout.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 8b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = "Medusa verify steps/s + tokens/s and achieved HBM GB/s at 8B shape, 1 GPU"
+
+WORKLOADS = {
+    "8b": "Medusa decode step, 8B-class shape: hidden 4096, vocab 128256, 4 heads with "
+          "top-(10,5,4,3), 64-node sparse tree, one-layer verifier with GQA 32 q / 8 kv heads "
+          "of dim 128, KV prefix 4096, batch 1",
+    "mid": "Medusa decode step, 7B-class shape: hidden 4096, vocab 32000, 5 heads with "
+           "top-(10,5,4,3,2), 64-node sparse tree, 32 heads of dim 128, KV prefix 1024, batch 1",
+    "dense": "Medusa decode step, 8B-class shape with the dense 256-node tree "
+             "(1+3+12+48+192), KV prefix 8192, batch 1",
+    "batched70b": "Medusa decode step, 70B-class shape: hidden 8192, vocab 32000, 5 heads, "
+                  "64-node sparse tree per sequence, GQA 64/8 x 128, batch 8, prefixes U[512,8192]",
+    "tiny": "Medusa decode step, worked-example shape: hidden 256, vocab 1000, 3 heads, fp32",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, n_nodes: int, prefix_total: int) -> dict:
+    """Bytes the method must move per step: every weight once, the valid KV rows, the
+    gathered embedding rows (read for Q/K/V and again for the residual)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    H, V, K = cfg.H, cfg.V, cfg.K
+    qd, kvd = cfg.Hq * cfg.d, cfg.Hkv * cfg.d
+    parts = {
+        "heads_ffn": K * H * H * es + K * H * es,
+        "heads_vocab": K * V * H * es,
+        "proxy_qkv": (qd + 2 * kvd) * H * es + cfg.B * n_nodes * H * es,
+        "attention": prefix_total * 2 * kvd * es,
+        "proxy_out": H * qd * es + cfg.B * n_nodes * H * es,
+        "verify_lmhead": V * H * es,
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def cpu_info():
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(inp, oplan) -> dict:
+    """The oracle, as it stands, on one full step of the same workload (host cores)."""
+    import oracle
+    t0 = time.perf_counter()
+    res = oracle.step(inp, oplan)
+    dt = time.perf_counter() - t0
+    cores, model = cpu_info()
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"one whole step (all parts) of the same workload and seed, fp64 numpy "
+                      f"({dt:.1f} s); host {model}, {cores} cores visible",
+            "seconds_per_step": dt, "accept_len": [int(a) for a in res.accept_len]}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from speculative_decoding_amd import medusa as M
+    from speculative_decoding_amd.step import Dims, MedusaStep, device_weights
+    from synth import get_config, make_inputs
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        return 1
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    patch = os.path.join(ROOT, "tests", "golden", "plants", f"{cfg.name}_s{args.seed}.json")
+    t0 = time.perf_counter()
+    inp = make_inputs(cfg, args.seed, patch=patch if os.path.exists(patch) else None)
+    log(f"[bench] generated {cfg.name} seed {args.seed} in {time.perf_counter() - t0:.1f} s "
+        f"(planted: {os.path.exists(patch)})")
+    w = device_weights(inp, dev)
+    if cfg.tree == "full":
+        plan = M.medusa_tree_plan_full(cfg.tree_s)
+    else:
+        plan = M.medusa_tree_plan_from_accuracy(inp.acc, cfg.tree_s, cfg.n_nodes)
+    plan.upload(dev)
+    n_nodes = plan.n_nodes
+    step = MedusaStep(Dims.from_config(cfg), w, plan, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] uploaded; tree {n_nodes} nodes, depth {plan.max_depth}")
+
+    # bootstrap root (not part of a steady-state step: there the root is the previous bonus)
+    step.heads(bootstrap_root=True)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step.run(bootstrap_root=False, keep_u=False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    # timed region: exactly K steps, per-kernel HIP events on the launch stream
+    M.medusa_profile_reset()
+    M.medusa_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run(bootstrap_root=False, keep_u=False)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    M.medusa_profile_enable(False)
+    kernels = {}
+    for name in ("heads_ffn", "heads_vocab", "heads_merge", "build_tree", "proxy_qkv",
+                 "attn_partial", "attn_combine", "proxy_out", "verify_lmhead", "verify_accept"):
+        ms, n = M.medusa_profile_query(name)
+        if n:
+            kernels[name] = {"avg_us": 1e3 * ms / n, "launches": n}
+    log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
+
+    res = step.results()
+    a = [int(x) for x in res["accept_len"]]
+    prefix_total = int(np.minimum(inp.prefix_lens, cfg.Lcap).sum())
+    ab = algorithmic_bytes(cfg, n_nodes, prefix_total)
+    sec = elapsed / args.steps
+    steps_per_s = 1.0 / sec
+    expect_a = 0.0
+    parent, depth, rank, _ = plan.arrays()
+    for i in range(1, n_nodes):
+        p, j = 1.0, i
+        while j > 0:
+            p *= float(inp.acc[depth[j] - 1, rank[j]])
+            j = parent[j]
+        expect_a += p
+    mean_a = float(np.mean(a))
+    hv = kernels.get("heads_vocab", {}).get("avg_us")
+    roof = None
+    if hv:
+        achieved = ab["heads_vocab"] / (hv * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "heads_vocab",
+                "bytes_per_launch": ab["heads_vocab"], "avg_us": hv}
+    out = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * sec,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded draws, planted head ranks; no trained weights)",
+        "config": {"workload": WORKLOADS[cfg.name], "name": cfg.name, "seed": args.seed,
+                   "batch": cfg.B, "tree_nodes": n_nodes, "prefix": cfg.L or list(map(int, inp.prefix_lens))},
+        "tokens_per_s": steps_per_s * cfg.B * (1.0 + mean_a),
+        "tokens_per_s_expected": steps_per_s * cfg.B * (1.0 + expect_a),
+        "accept_len": a,
+        "expected_accept_len": expect_a,
+        "hbm_gbps": ab["total"] / sec / 1e9,
+        "hbm_frac": ab["total"] / sec / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": ab["total"],
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from tests.planting import plan_for
+        log("[bench] timing the CPU oracle on one step")
+        out["cpu_baseline"] = cpu_baseline(inp, plan_for(cfg, inp.acc))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -10,7 +10,9 @@
 // are computed transposed, S^T = K Q^T, so each lane owns one query row; its softmax
 // state stays in registers and the value sum O^T = V^T P^T takes P^T straight from the
 // score registers (the two 16-key score tiles give each lane the eight key slots of one
-// 32-deep MFMA step; V^T is read from LDS with the same key order).  Partial (max, sum,
+// 32-deep MFMA step; V^T is read from LDS with the same key order).  For bf16 the
+// probabilities enter that MFMA as a hi + lo pair of bf16 values, so rounding them costs
+// no more than fp32 accumulation would.  Partial (max, sum,
 // unnormalised output) per key range go to the workspace; a second kernel combines them.
 // The ancestor mask is one 64-bit word per (node, 64 keys).
 #include "common.hpp"
@@ -46,13 +48,22 @@ template <> struct Vt4<bf16_t> {
         const uint2 b = *reinterpret_cast<const uint2*>(p1);
         f.v = u32x4{a.x, a.y, b.x, b.y};
     }
-    __device__ static __forceinline__ void pack(Frag<bf16_t>& f, const float* p) {
-        uint32_t w[4];
+    // p ~= hi + lo with hi = bf16(p) and lo = bf16(p - hi): the value sum runs as two
+    // bf16 MFMAs, so the probabilities keep about 16 significant bits instead of 8.
+    __device__ static __forceinline__ void pack(Frag<bf16_t>& hi, Frag<bf16_t>& lo, const float* p) {
+        uint32_t wh[4], wl[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)f32_to_bf16(p[2 * i]) | ((uint32_t)f32_to_bf16(p[2 * i + 1]) << 16);
-        f.v = u32x4{w[0], w[1], w[2], w[3]};
+        for (int i = 0; i < 4; ++i) {
+            const bf16_t h0 = f32_to_bf16(p[2 * i]), h1 = f32_to_bf16(p[2 * i + 1]);
+            const bf16_t l0 = f32_to_bf16(p[2 * i] - bf16_to_f32(h0));
+            const bf16_t l1 = f32_to_bf16(p[2 * i + 1] - bf16_to_f32(h1));
+            wh[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            wl[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        hi.v = u32x4{wh[0], wh[1], wh[2], wh[3]};
+        lo.v = u32x4{wl[0], wl[1], wl[2], wl[3]};
     }
+    static constexpr bool kSplit = true;
     __device__ static __forceinline__ bf16_t elem(const u32x4& v, int e) {
         const uint32_t w = v[e >> 1];
         return (bf16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
@@ -63,10 +74,12 @@ template <> struct Vt4<float> {
         f.lo = *reinterpret_cast<const u32x4*>(p0);
         f.hi = *reinterpret_cast<const u32x4*>(p1);
     }
-    __device__ static __forceinline__ void pack(Frag<float>& f, const float* p) {
+    __device__ static __forceinline__ void pack(Frag<float>& f, Frag<float>& unused, const float* p) {
         f.lo = u32x4{__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3])};
         f.hi = u32x4{__float_as_uint(p[4]), __float_as_uint(p[5]), __float_as_uint(p[6]), __float_as_uint(p[7])};
+        unused.zero();
     }
+    static constexpr bool kSplit = false;
     __device__ static __forceinline__ float elem(const u32x4& v, int e) { return __uint_as_float(v[e]); }
 };
 
@@ -132,23 +145,39 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    for (int kb0 = k_begin; kb0 < k_end; kb0 += kKeys) {
-        __syncthreads();
-        constexpr int VPR = D / EPV;     // 16-byte vectors per key row
-        for (int idx = threadIdx.x; idx < kKeys * VPR; idx += kThreads) {
+    // K/V blocks are fetched into registers one block ahead, so the global loads of block
+    // j+1 are in flight while block j is multiplied out of LDS.
+    constexpr int VPR = D / EPV;                 // 16-byte vectors per key row
+    constexpr int NV = kKeys * VPR / kThreads;   // vectors per thread per block
+    u32x4 kr[NV], vr[NV];
+    auto fetch = [&](int kb0) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int idx = threadIdx.x + j * kThreads;
             const int key = idx / VPR;
             const int c = idx - key * VPR;
-            u32x4 kv = u32x4{0u, 0u, 0u, 0u};
-            u32x4 vv = kv;
+            kr[j] = u32x4{0u, 0u, 0u, 0u};
+            vr[j] = kr[j];
             if (kb0 + key < k_end) {
-                kv = *reinterpret_cast<const u32x4*>(ksrc + (long long)(kb0 + key) * kstride + c * EPV);
-                vv = *reinterpret_cast<const u32x4*>(vsrc + (long long)(kb0 + key) * kstride + c * EPV);
+                kr[j] = *reinterpret_cast<const u32x4*>(ksrc + (long long)(kb0 + key) * kstride + c * EPV);
+                vr[j] = *reinterpret_cast<const u32x4*>(vsrc + (long long)(kb0 + key) * kstride + c * EPV);
             }
-            *reinterpret_cast<u32x4*>(Ks + key * KP + c * EPV) = kv;
+        }
+    };
+    fetch(k_begin);
+    for (int kb0 = k_begin; kb0 < k_end; kb0 += kKeys) {
+        __syncthreads();
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) Vt[(c * EPV + e) * VP + key] = Vt4<T>::elem(vv, e);
+        for (int j = 0; j < NV; ++j) {
+            const int idx = threadIdx.x + j * kThreads;
+            const int key = idx / VPR;
+            const int c = idx - key * VPR;
+            *reinterpret_cast<u32x4*>(Ks + key * KP + c * EPV) = kr[j];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) Vt[(c * EPV + e) * VP + key] = Vt4<T>::elem(vr[j], e);
         }
         __syncthreads();
+        if (kb0 + kKeys < k_end) fetch(kb0 + kKeys);
         uint64_t mword = ~0ull;
         if (tree) mword = row_ok ? a.plan.mask[(long long)node * a.plan.mask_words + (kb0 >> 6)] : 0ull;
 
@@ -197,8 +226,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
             for (int e = 0; e < 8; ++e) psum += p[e];
             l_run = l_run * alpha + psum;
             m_run = m_new;
-            Frag<T> pf;
-            Vt4<T>::pack(pf, p);
+            Frag<T> pf, pf_lo;
+            Vt4<T>::pack(pf, pf_lo, p);
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
                 o[t] *= alpha;
@@ -206,6 +235,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
                 const T* vrow = Vt + (t * 16 + ln) * VP + kb + 4 * lg;
                 Vt4<T>::load2(vf, vrow, vrow + 16);
                 mma(o[t], vf, pf);
+                if (Vt4<T>::kSplit) mma(o[t], vf, pf_lo);
             }
         }
     }
@@ -240,23 +270,49 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnArgs a
     const int n_slots = sh.n_splits + 1;
     const int L = min(max(a.prefix_lens[b], 0), sh.Lcap);
 
-    float mx = -INFINITY;
-    for (int s = 0; s < n_slots; ++s) {
-        if (s < sh.n_splits && s * sh.chunk >= L) continue;
-        const long long base = (((long long)b * sh.Hkv + g) * n_slots + s) * sh.rows + r;
-        mx = fmaxf(mx, a.ws_ml[base * 2]);
-    }
+    // every lane fetches one slot's (max, sum) so the slots are read in parallel
+    const long long base0 = (((long long)b * sh.Hkv + g) * n_slots) * sh.rows + r;
     float den = 0.f;
     float num[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) num[e] = 0.f;
-    for (int s = 0; s < n_slots; ++s) {
-        if (s < sh.n_splits && s * sh.chunk >= L) continue;
-        const long long base = (((long long)b * sh.Hkv + g) * n_slots + s) * sh.rows + r;
-        const float w = exp2f(a.ws_ml[base * 2] - mx);
-        den += w * a.ws_ml[base * 2 + 1];
+    float mx = -INFINITY;
+    for (int s0 = 0; s0 < n_slots; s0 += kWave) {
+        const int s = s0 + lane;
+        const bool live = s < n_slots && (s == sh.n_splits || s * sh.chunk < L);
+        const float ms = live ? a.ws_ml[(base0 + (long long)s * sh.rows) * 2] : -INFINITY;
+        float m = ms;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] += w * a.ws_o[base * D + lane + kWave * e];
+        for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, shfl_xor_f(m, o));
+        mx = fmaxf(mx, m);
+    }
+    for (int s0 = 0; s0 < n_slots; s0 += kWave) {
+        const int s = s0 + lane;
+        const bool live = s < n_slots && (s == sh.n_splits || s * sh.chunk < L);
+        const long long bs = base0 + (long long)s * sh.rows;
+        const float w = live ? exp2f(a.ws_ml[bs * 2] - mx) : 0.f;
+        float part = live ? w * a.ws_ml[bs * 2 + 1] : 0.f;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) part += shfl_xor_f(part, o);
+        den += part;
+        const int cnt = min(kWave, n_slots - s0);
+        for (int j0 = 0; j0 < cnt; j0 += 8) {
+            float ov[8][PER];
+            float wj[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                wj[j] = __shfl(w, (j0 + j) & (kWave - 1), kWave);
+                const bool use = j0 + j < cnt && wj[j] != 0.f;
+                const long long bj = base0 + (long long)(s0 + j0 + j) * sh.rows;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) ov[j][e] = use ? a.ws_o[bj * D + lane + kWave * e] : 0.f;
+                if (!use) wj[j] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < PER; ++e) num[e] += wj[j] * ov[j][e];
+        }
     }
     const float inv = 1.f / den;
     T* out = static_cast<T*>(a.out) + (((long long)b * sh.N + i) * sh.Hq + j) * D;

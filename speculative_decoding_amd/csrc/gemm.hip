@@ -22,12 +22,185 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kLdsXBytes = 32768;     // X chunk budget
-constexpr int kUnroll = 4;            // k-steps whose W loads are issued together
+constexpr int kLdsXBytes = 40960;     // X chunk budget (bytes of LDS)
+constexpr int kSplitUnroll = 4;       // k-steps per load group in the split-contraction kernel
 
-template <typename T> constexpr int rt_for() { return sizeof(T) == 2 ? 4 : 2; }
+// Streaming-kernel tiles: RT 16-row weight tiles per wave, UN k-steps per load group.
+// Chosen by a sweep on MI355X at the 8B shape (RT in {1,2,4} x UN in {2,4,8}): the
+// top-s (heads) launch is flat within a few percent across the sweep, the argmax
+// (verify) launch prefers short groups.
+template <typename T, int EPI> struct StreamCfg { static constexpr int RT = 2, UN = 4; };
+template <> struct StreamCfg<bf16_t, EPI_TOPS> { static constexpr int RT = 2, UN = 8; };
+template <> struct StreamCfg<bf16_t, EPI_ARGMAX> { static constexpr int RT = 2, UN = 2; };
 
-template <typename T, int MT, int RT, int EPI>
+// acc[rt][mt][r] = Y[m0 + mt*16 + 4*lg + r][n_wave + rt*16 + ln]:
+// out[m][n] = rnd(silu?(Y + bias[n]) + residual[m][n]).
+template <typename T, int MT, int RT>
+__device__ __forceinline__ void store_epilogue(const GemmProblem& P, const GemmBatch& bt,
+                                               const floatx4 (&acc)[RT][MT], int m0, int n_wave,
+                                               int ln, int lg) {
+    using E = Elem<T>;
+    T* out = static_cast<T*>(P.out);
+    const T* bias = static_cast<const T*>(P.bias);
+    const T* res = static_cast<const T*>(P.res);
+    const int N = P.N;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int n = n_wave + rt * 16 + ln;
+        if (n >= N) continue;
+        const float bn = bias ? E::to_f32(bias[n]) : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + mt * 16 + 4 * lg + r;
+                if (m >= bt.M) continue;
+                float y = acc[rt][mt][r] + bn;
+                if (P.silu) y = silu(y);
+                if (res) {
+                    long long rr = m;
+                    bool ok = true;
+                    if (P.res_rows) {
+                        rr = P.res_rows[m];
+                        ok = rr >= 0 && rr < bt.res_rows_bound;
+                    }
+                    if (ok) y += E::to_f32(res[rr * P.res_stride + n]);
+                }
+                out[(long long)m * P.ldo + n] = E::from_f32(y);
+            }
+    }
+}
+
+// Problem lookup: the last problem whose first tile is <= t.
+__device__ __forceinline__ int problem_of(const GemmBatch& bt, int t) {
+    int pi = 0;
+    while (pi + 1 < bt.n_problems && t >= bt.p[pi + 1].tile_begin) ++pi;
+    return pi;
+}
+
+// Few weight rows (up to ~16K) and up to 64 input rows: all four waves of a workgroup take
+// the same RT*16 weight rows and split the contraction into four contiguous quarters, so a
+// small projection still spreads over hundreds of workgroups.  X fragments are read straight
+// from global memory (each wave uses only its own quarter, so LDS staging would buy no
+// reuse); the four partial accumulators are summed in a fixed order through LDS.
+template <typename T, int MT, int RT>
+__global__ __launch_bounds__(kThreads) void gemm_splitk_store_kernel(const GemmBatch bt) {
+    constexpr int KS = kWaves;
+    __shared__ floatx4 red[KS - 1][RT][MT][kWave];
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    const int nblocks = bt.total_tiles * n_mb;
+    const int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int mb = bid % n_mb;
+    const int t = bid / n_mb;
+    const GemmProblem& P = bt.p[problem_of(bt, t)];
+    const int tile = t - P.tile_begin;
+    const int K = bt.K;
+    const int N = P.N;
+    const int kg = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int n_wave = tile * RT * 16;
+    const int m0 = mb * MT * 16;
+
+    const int steps = K / 32;
+    const int per = (steps + KS - 1) / KS;
+    const int k_lo = min(K, kg * per * 32);
+    const int k_hi = min(K, (kg + 1) * per * 32);
+
+    const T* W = static_cast<const T*>(P.W);
+    const T* wrow[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        wrow[rt] = W + (long long)min(n_wave + rt * 16 + ln, N - 1) * K + 8 * lg;
+    const T* X = static_cast<const T*>(P.X);
+    const T* xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = m0 + mt * 16 + ln;
+        long long r = m;
+        bool ok = m < bt.M;
+        if (ok && P.x_rows) {
+            r = P.x_rows[m];
+            ok = r >= 0 && r < bt.x_rows_bound;
+        }
+        xrow[mt] = ok ? X + r * P.x_stride + 8 * lg : nullptr;
+    }
+
+    floatx4 acc[RT][MT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto load = [&](Frag<T> (&wf)[kSplitUnroll][RT], Frag<T> (&xf)[kSplitUnroll][MT], int k) {
+#pragma unroll
+        for (int u = 0; u < kSplitUnroll; ++u) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) wf[u][rt].load(wrow[rt] + k + 32 * u);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if (xrow[mt]) xf[u][mt].load(xrow[mt] + k + 32 * u);
+                else xf[u][mt].zero();
+            }
+        }
+    };
+    auto compute = [&](const Frag<T> (&wf)[kSplitUnroll][RT], const Frag<T> (&xf)[kSplitUnroll][MT]) {
+#pragma unroll
+        for (int u = 0; u < kSplitUnroll; ++u)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) mma(acc[rt][mt], xf[u][mt], wf[u][rt]);
+    };
+    // software pipeline: group g+1's loads are in flight while group g is multiplied
+    constexpr int GK = 32 * kSplitUnroll;
+    const int G = (k_hi - k_lo) / GK;
+    Frag<T> wa[kSplitUnroll][RT], wb[kSplitUnroll][RT];
+    Frag<T> xa[kSplitUnroll][MT], xb[kSplitUnroll][MT];
+    if (G > 0) load(wa, xa, k_lo);
+    for (int g = 0; g < G; g += 2) {
+        if (g + 1 < G) load(wb, xb, k_lo + (g + 1) * GK);
+        compute(wa, xa);
+        if (g + 1 < G) {
+            if (g + 2 < G) load(wa, xa, k_lo + (g + 2) * GK);
+            compute(wb, xb);
+        }
+    }
+    for (int k = k_lo + G * GK; k < k_hi; k += 32) {
+        Frag<T> wf[RT];
+        Frag<T> xf[MT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) wf[rt].load(wrow[rt] + k);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (xrow[mt]) xf[mt].load(xrow[mt] + k);
+            else xf[mt].zero();
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) mma(acc[rt][mt], xf[mt], wf[rt]);
+    }
+
+    if (kg > 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) red[kg - 1][rt][mt][lane] = acc[rt][mt];
+    }
+    __syncthreads();
+    if (kg != 0) return;
+#pragma unroll
+    for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[rt][mt] += red[w][rt][mt][lane];
+    store_epilogue<T, MT, RT>(P, bt, acc, m0, n_wave, ln, lg);
+}
+
+template <typename T, int MT, int RT, int UN, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
     using E = Elem<T>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -41,9 +214,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
     const int bid = xcd_logical_block(blockIdx.x, nblocks);
     const int mb = bid % n_mb;
     const int t = bid / n_mb;
-    int pi = 0;
-    while (pi + 1 < bt.n_problems && t >= bt.p[pi + 1].tile_begin) ++pi;
-    const GemmProblem& P = bt.p[pi];
+    const GemmProblem& P = bt.p[problem_of(bt, t)];
     const int tile = t - P.tile_begin;
     const int K = bt.K;
     const int N = P.N;
@@ -71,13 +242,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
         for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     T* xs = reinterpret_cast<T*>(smem);
-    const int KC = bt.KC;
+    const int KC = bt.KC;               // a multiple of 32 * UN unless K is smaller
     const int pitch = KC + 8;
     const T* X = static_cast<const T*>(P.X);
+    int kc_staged = -1;
 
-    for (int kc = 0; kc < K; kc += KC) {
-        const int klen = min(KC, K - kc);
+    // Stage X[m0 .. m0+Mb)[kc .. kc+KC) into LDS (all threads; uniform call).
+    auto stage = [&](int kc) {
         __syncthreads();
+        const int klen = min(KC, K - kc);
         const int per_row = klen / EPV;
         for (int idx = threadIdx.x; idx < Mb * per_row; idx += kThreads) {
             const int m = idx / per_row;
@@ -94,77 +267,70 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
             *reinterpret_cast<u32x4*>(xs + m * pitch + c * EPV) = v;
         }
         __syncthreads();
-
-        int ks = 0;
-        for (; ks + 32 * kUnroll <= klen; ks += 32 * kUnroll) {
-            Frag<T> wf[kUnroll][RT];
+        kc_staged = kc;
+    };
+    auto load_w = [&](Frag<T> (&wf)[UN][RT], int k) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < UN; ++u)
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) wf[u][rt].load(wrow[rt] + kc + ks + 32 * u);
+            for (int rt = 0; rt < RT; ++rt) wf[u][rt].load(wrow[rt] + k + 32 * u);
+    };
+    auto compute = [&](const Frag<T> (&wf)[UN][RT], int k) {
+        const int c = k / KC * KC;
+        if (c != kc_staged) stage(c);
+        const int kl = k - c;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                Frag<T> xf[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const int m = mt * 16 + ln;
-                    if (m < Mb) xf[mt].load(xs + m * pitch + ks + 32 * u + 8 * lg);
-                    else xf[mt].zero();
-                }
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) mma(acc[rt][mt], xf[mt], wf[u][rt]);
-            }
-        }
-        for (; ks < klen; ks += 32) {
-            Frag<T> wf[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) wf[rt].load(wrow[rt] + kc + ks);
+        for (int u = 0; u < UN; ++u) {
             Frag<T> xf[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = mt * 16 + ln;
-                if (m < Mb) xf[mt].load(xs + m * pitch + ks + 8 * lg);
+                if (m < Mb) xf[mt].load(xs + m * pitch + kl + 32 * u + 8 * lg);
                 else xf[mt].zero();
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) mma(acc[rt][mt], xf[mt], wf[rt]);
+                for (int mt = 0; mt < MT; ++mt) mma(acc[rt][mt], xf[mt], wf[u][rt]);
         }
+    };
+
+    // Software pipeline over groups of UN k-steps: the W loads of group g+1 are in
+    // flight while group g is multiplied.
+    constexpr int GK = 32 * UN;
+    const int G = K / GK;
+    Frag<T> wa[UN][RT], wb[UN][RT];
+    if (G > 0) load_w(wa, 0);
+    for (int g = 0; g < G; g += 2) {
+        if (g + 1 < G) load_w(wb, (g + 1) * GK);
+        compute(wa, g * GK);
+        if (g + 1 < G) {
+            if (g + 2 < G) load_w(wa, (g + 2) * GK);
+            compute(wb, (g + 1) * GK);
+        }
+    }
+    for (int k = G * GK; k < K; k += 32) {
+        const int c = k / KC * KC;
+        if (c != kc_staged) stage(c);
+        Frag<T> wf[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) wf[rt].load(wrow[rt] + k);
+        Frag<T> xf[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mt * 16 + ln;
+            if (m < Mb) xf[mt].load(xs + m * pitch + (k - c) + 8 * lg);
+            else xf[mt].zero();
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) mma(acc[rt][mt], xf[mt], wf[rt]);
     }
 
     // acc[rt][mt][r] = Y[m0 + mt*16 + 4*lg + r][n_wave + rt*16 + ln]
     if (EPI == EPI_STORE) {
-        T* out = static_cast<T*>(P.out);
-        const T* bias = static_cast<const T*>(P.bias);
-        const T* res = static_cast<const T*>(P.res);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int n = n_wave + rt * 16 + ln;
-            if (n >= N) continue;
-            const float bn = bias ? E::to_f32(bias[n]) : 0.f;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + mt * 16 + 4 * lg + r;
-                    if (m >= bt.M) continue;
-                    float y = acc[rt][mt][r] + bn;
-                    if (P.silu) y = silu(y);
-                    if (res) {
-                        long long rr = m;
-                        bool ok = true;
-                        if (P.res_rows) {
-                            rr = P.res_rows[m];
-                            ok = rr >= 0 && rr < bt.res_rows_bound;
-                        }
-                        if (ok) y += E::to_f32(res[rr * P.res_stride + n]);
-                    }
-                    out[(long long)m * P.ldo + n] = E::from_f32(y);
-                }
-        }
+        store_epilogue<T, MT, RT>(P, bt, acc, m0, n_wave, ln, lg);
         return;
     }
 
@@ -265,9 +431,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
 }
 
 // k-way merge of the per-tile candidate lists (each sorted best first) into the top-s.
+// The lists are first copied to LDS when they fit, so each round costs one block-wide
+// reduction; the wave winners alternate between two LDS slots so one barrier per round
+// suffices.
+constexpr int kMergeLdsEntries = 12288;  // 96 KB of (value, id) pairs
+
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch bt) {
-    __shared__ float sv[kWaves];
-    __shared__ int si[kWaves];
+    extern __shared__ __align__(16) unsigned char msmem[];
+    float* lv = reinterpret_cast<float*>(msmem);
+    int* li = reinterpret_cast<int*>(lv + kMergeLdsEntries);
+    __shared__ float sv[2][kWaves];
+    __shared__ int si[2][kWaves];
     constexpr int kMaxOwned = 8;
     const int p = blockIdx.x / bt.M;
     const int m = blockIdx.x - p * bt.M;
@@ -277,6 +451,31 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch b
     const int32_t* pi = P.part_idx + (long long)m * P.n_tiles * s;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int total = P.n_tiles * s;
+    const bool in_lds = total <= kMergeLdsEntries;
+    if (in_lds) {
+        // eight independent loads per thread in flight before the LDS stores
+        for (int base = threadIdx.x; base < total; base += 8 * kThreads) {
+            float v[8];
+            int id[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = base + j * kThreads;
+                v[j] = i < total ? pv[i] : 0.f;
+                id[j] = i < total ? pi[i] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = base + j * kThreads;
+                if (i < total) { lv[i] = v[j]; li[i] = id[j]; }
+            }
+        }
+        __syncthreads();
+    }
+    auto fetch = [&](int idx, float& v, int& id) {
+        if (in_lds) { v = lv[idx]; id = li[idx]; }
+        else { v = pv[idx]; id = pi[idx]; }
+    };
 
     int ptr[kMaxOwned];
     float hv[kMaxOwned];
@@ -285,13 +484,9 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch b
     for (int j = 0; j < kMaxOwned; ++j) {
         const int tl = threadIdx.x + j * kThreads;
         ptr[j] = 0;
-        if (tl < P.n_tiles) {
-            hv[j] = pv[(long long)tl * s];
-            hi[j] = pi[(long long)tl * s];
-        } else {
-            hv[j] = -INFINITY;
-            hi[j] = INT_MAX;
-        }
+        hv[j] = -INFINITY;
+        hi[j] = INT_MAX;
+        if (tl < P.n_tiles) fetch(tl * s, hv[j], hi[j]);
     }
     for (int round = 0; round < s; ++round) {
         float bv = -INFINITY;
@@ -301,14 +496,14 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch b
             if (better(hv[j], hi[j], bv, bi)) { bv = hv[j]; bi = hi[j]; }
         const int mine = bi;
         reduce_best<kWave>(bv, bi);
-        if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
+        const int slot = round & 1;
+        if (lane == 0) { sv[slot][wave] = bv; si[slot][wave] = bi; }
         __syncthreads();
-        bv = sv[0];
-        bi = si[0];
+        bv = sv[slot][0];
+        bi = si[slot][0];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
-            if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
-        __syncthreads();
+            if (better(sv[slot][w], si[slot][w], bv, bi)) { bv = sv[slot][w]; bi = si[slot][w]; }
         if (threadIdx.x == 0) {
             P.out_ids[(long long)m * P.out_ld + round] = bi == INT_MAX ? -1 : bi;
             if (P.out_vals) P.out_vals[(long long)m * P.out_ld + round] = bv;
@@ -319,13 +514,9 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch b
                 if (hi[j] == bi) {
                     const int tl = threadIdx.x + j * kThreads;
                     ++ptr[j];
-                    if (ptr[j] < s) {
-                        hv[j] = pv[(long long)tl * s + ptr[j]];
-                        hi[j] = pi[(long long)tl * s + ptr[j]];
-                    } else {
-                        hv[j] = -INFINITY;
-                        hi[j] = INT_MAX;
-                    }
+                    hv[j] = -INFINITY;
+                    hi[j] = INT_MAX;
+                    if (ptr[j] < s) fetch(tl * s + ptr[j], hv[j], hi[j]);
                 }
             }
         }
@@ -338,10 +529,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch b
 
 template <typename T, int MT, int EPI>
 hipError_t launch_t(GemmBatch& bt, hipStream_t stream) {
-    constexpr int RT = rt_for<T>();
+    constexpr int RT = StreamCfg<T, EPI>::RT;
+    constexpr int UN = StreamCfg<T, EPI>::UN;
     const int mrows = min(bt.M, MT * 16);
-    int kc = (kLdsXBytes / (mrows * (int)sizeof(T)) - 8) / 32 * 32;
-    kc = max(32, min(kc, (bt.K + 31) / 32 * 32));
+    constexpr int GK = 32 * UN;
+    int kc = (kLdsXBytes / (mrows * (int)sizeof(T)) - 8) / GK * GK;
+    kc = max(GK, min(kc, (bt.K + GK - 1) / GK * GK));
     bt.KC = kc;
     size_t lds = (size_t)mrows * (kc + 8) * sizeof(T);
     if (EPI == EPI_TOPS) {
@@ -350,8 +543,26 @@ hipError_t launch_t(GemmBatch& bt, hipStream_t stream) {
     }
     const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
     dim3 grid(bt.total_tiles * n_mb);
-    hipLaunchKernelGGL((gemm_kernel<T, MT, RT, EPI>), grid, dim3(kThreads), lds, stream, bt);
+    hipLaunchKernelGGL((gemm_kernel<T, MT, RT, UN, EPI>), grid, dim3(kThreads), lds, stream, bt);
     return hipGetLastError();
+}
+
+template <typename T, int MT, int RT>
+hipError_t launch_splitk(GemmBatch& bt, hipStream_t stream) {
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    hipLaunchKernelGGL((gemm_splitk_store_kernel<T, MT, RT>), dim3(bt.total_tiles * n_mb),
+                       dim3(kThreads), 0, stream, bt);
+    return hipGetLastError();
+}
+
+// Weight rows per workgroup of the split-contraction store kernel.
+int splitk_rt(int M) { return M <= 16 ? 2 : 1; }
+
+template <typename T>
+hipError_t launch_store(GemmBatch& bt, hipStream_t stream) {
+    if (bt.M <= 16) return launch_splitk<T, 1, 2>(bt, stream);
+    if (bt.M <= 32) return launch_splitk<T, 2, 1>(bt, stream);
+    return launch_splitk<T, 4, 1>(bt, stream);
 }
 
 template <typename T, int EPI>
@@ -364,7 +575,7 @@ hipError_t launch_mt(GemmBatch& bt, hipStream_t stream) {
 template <typename T>
 hipError_t launch_epi(int epi, GemmBatch& bt, hipStream_t stream) {
     switch (epi) {
-        case EPI_STORE: return launch_mt<T, EPI_STORE>(bt, stream);
+        case EPI_STORE: return launch_store<T>(bt, stream);
         case EPI_TOPS: return launch_mt<T, EPI_TOPS>(bt, stream);
         default: return launch_mt<T, EPI_ARGMAX>(bt, stream);
     }
@@ -372,8 +583,14 @@ hipError_t launch_epi(int epi, GemmBatch& bt, hipStream_t stream) {
 
 }  // namespace
 
-int gemm_rows_per_tile(medusa_dtype dt, int /*M*/, int /*epi*/) {
-    return kWaves * 16 * (dt == MEDUSA_BF16 ? rt_for<bf16_t>() : rt_for<float>());
+int gemm_rows_per_tile(medusa_dtype dt, int M, int epi) {
+    if (epi == EPI_STORE) return 16 * splitk_rt(M);
+    int rt;
+    if (dt == MEDUSA_BF16)
+        rt = epi == EPI_TOPS ? StreamCfg<bf16_t, EPI_TOPS>::RT : StreamCfg<bf16_t, EPI_ARGMAX>::RT;
+    else
+        rt = epi == EPI_TOPS ? StreamCfg<float, EPI_TOPS>::RT : StreamCfg<float, EPI_ARGMAX>::RT;
+    return kWaves * 16 * rt;
 }
 
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& bt, hipStream_t stream) {
@@ -381,7 +598,8 @@ hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& bt, hipStream_t stre
 }
 
 hipError_t topk_merge_launch(const MergeBatch& bt, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(bt.n_problems * bt.M), dim3(kThreads), 0, stream, bt);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(bt.n_problems * bt.M), dim3(kThreads),
+                       kMergeLdsEntries * (sizeof(float) + sizeof(int)), stream, bt);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void build_tree_kernel(DevicePlan plan, int K,
     if (position_ids) position_ids[(long long)b * N + i] = (prefix_lens ? prefix_lens[b] : 0) + d;
 }
 
-constexpr int kAcceptThreads = 256;
+constexpr int kAcceptThreads = 1024;
 constexpr int kMaxNodes = MEDUSA_MAX_NODES;
 
 // One workgroup per sequence: merge the lm_head argmax partials of every node, then walk
@@ -50,21 +50,33 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const int b = blockIdx.x;
     const int N = plan.n_nodes;
     const int D = plan.max_depth;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    constexpr int kWaves = kAcceptThreads / kWave;
-
-    for (int i = wave; i < N; i += kWaves) {
-        const long long base = ((long long)b * N + i) * n_tiles;
+    // 16 lanes per node: each lane scans a strided share of the node's tile partials with
+    // eight loads in flight, then the 16 lanes reduce.
+    constexpr int kPerNode = 16;
+    for (int i0 = 0; i0 < N; i0 += kAcceptThreads / kPerNode) {
+        const int i = i0 + threadIdx.x / kPerNode;
+        const int sub = threadIdx.x % kPerNode;
         float bv = -INFINITY;
         int bi = INT_MAX;
-        for (int t = lane; t < n_tiles; t += kWave) {
-            const float v = part_val[base + t];
-            const int id = part_idx[base + t];
-            if (better(v, id, bv, bi)) { bv = v; bi = id; }
+        if (i < N) {
+            const float* pv = part_val + ((long long)b * N + i) * n_tiles;
+            const int32_t* pi = part_idx + ((long long)b * N + i) * n_tiles;
+            for (int t0 = sub; t0 < n_tiles; t0 += 8 * kPerNode) {
+                float v[8];
+                int id[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = t0 + j * kPerNode;
+                    v[j] = t < n_tiles ? pv[t] : -INFINITY;
+                    id[j] = t < n_tiles ? pi[t] : INT_MAX;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
+            }
         }
-        reduce_best<kWave>(bv, bi);
-        if (lane == 0) {
+        reduce_best<kPerNode>(bv, bi);
+        if (sub == 0 && i < N) {
             s_arg[i] = bi;
             if (node_argmax) node_argmax[(long long)b * N + i] = bi;
         }

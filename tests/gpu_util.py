@@ -77,7 +77,7 @@ def gpu_plan(inp, device):
     return p.upload(device)
 
 
-def run_gpu(inp, device, keep_logits=True, bootstrap_root=True, root=None):
+def run_gpu(inp, device, keep_logits=True, bootstrap_root=True, root=None, keep_u=True):
     import torch
     from speculative_decoding_amd.step import Dims, MedusaStep, device_weights
     plan = gpu_plan(inp, device)
@@ -85,12 +85,13 @@ def run_gpu(inp, device, keep_logits=True, bootstrap_root=True, root=None):
                       keep_logits=keep_logits)
     if root is not None:
         step.root_ids.copy_(torch.as_tensor(np.asarray(root, np.int32), device=device))
-    step.run(bootstrap_root=bootstrap_root)
+    step.run(bootstrap_root=bootstrap_root, keep_u=keep_u)
     torch.cuda.synchronize()
     return step, step.results()
 
 
-def compare_step(inp, got: dict, ref: "oracle.StepResult", check_logits: bool = True) -> None:
+def compare_step(inp, got: dict, ref: "oracle.StepResult", check_logits: bool = True,
+                 check_u: bool = True) -> None:
     """Every output of the GPU step against the oracle; reports all mismatches at once.
     Ids, tokens and accept results bit-exact; floating outputs within tolerance."""
     cfg = inp.cfg
@@ -103,13 +104,14 @@ def compare_step(inp, got: dict, ref: "oracle.StepResult", check_logits: bool = 
         lambda: exact("accept_len", got["accept_len"], ref.accept_len),
         lambda: exact("accept_nodes", got["accept_nodes"], ref.accept_nodes),
         lambda: exact("accept_tokens", got["accept_tokens"], ref.accept_tokens),
-        lambda: close("u", got["u"], ref.u),
         lambda: close("q", got["q"], ref.q),
         lambda: close("k_tree", got["k_tree"], ref.k),
         lambda: close("v_tree", got["v_tree"], ref.v),
         lambda: close("o", got["o"], ref.o),
         lambda: close("node_hidden", got["node_hidden"], ref.node_hidden),
     ]
+    if check_u:
+        checks.append(lambda: close("u", got["u"], ref.u))
     for k in range(cfg.K):
         sk = cfg.s[k]
         checks.append(lambda k=k, sk=sk: close(f"topk_vals[head {k}]", got["topk_vals"][:, k, :sk],
