@@ -20,8 +20,8 @@ size_t esize(medusa_dtype dt) { return dt == MEDUSA_BF16 ? 2 : 4; }
 bool dtype_ok(medusa_dtype dt) { return dt == MEDUSA_BF16 || dt == MEDUSA_F32; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-int n_tiles_for(medusa_dtype dt, int M, int epi, int N) {
-    const int rows = gemm_rows_per_tile(dt, M, epi);
+int n_tiles_for(medusa_dtype dt, int M, int epi, int N, int K) {
+    const int rows = gemm_rows_per_tile(dt, M, epi, K);
     return (N + rows - 1) / rows;
 }
 
@@ -45,7 +45,7 @@ HeadsLayout heads_layout(medusa_dtype dt, int B, int H, int V, int K, int s_max,
     HeadsLayout L;
     Carver c;
     if (with_u) L.u = c.take((size_t)B * K * H * esize(dt));
-    L.n_tiles = n_tiles_for(dt, B, EPI_TOPS, V);
+    L.n_tiles = n_tiles_for(dt, B, EPI_TOPS, V, H);
     for (int p = 0; p <= K; ++p) {
         const size_t n = (size_t)B * L.n_tiles * (p < K ? s_max : 1);
         L.part_val[p] = c.take(n * sizeof(float));
@@ -60,10 +60,10 @@ struct VerifyLayout {
     int n_tiles = 0;
 };
 
-VerifyLayout verify_layout(medusa_dtype dt, int M, int V) {
+VerifyLayout verify_layout(medusa_dtype dt, int M, int V, int H) {
     VerifyLayout L;
     Carver c;
-    L.n_tiles = n_tiles_for(dt, M, EPI_ARGMAX, V);
+    L.n_tiles = n_tiles_for(dt, M, EPI_ARGMAX, V, H);
     L.part_val = c.take((size_t)M * L.n_tiles * sizeof(float));
     L.part_idx = c.take((size_t)M * L.n_tiles * sizeof(int32_t));
     L.total = c.off;
@@ -160,7 +160,7 @@ medusa_status medusa_heads_forward(medusa_dtype dt, int B, int H, int V, int K,
     ffn.n_problems = K;
     ffn.M = B;
     ffn.K = H;
-    const int ffn_tiles = n_tiles_for(dt, B, EPI_STORE, H);
+    const int ffn_tiles = n_tiles_for(dt, B, EPI_STORE, H, H);
     for (int k = 0; k < K; ++k) {
         GemmProblem& p = ffn.p[k];
         p.W = static_cast<const unsigned char*>(w1) + (size_t)k * H * H * es;
@@ -297,7 +297,7 @@ medusa_status medusa_tree_attention(const medusa_tree_plan* plan, medusa_dtype d
 
 size_t medusa_verify_workspace(const medusa_tree_plan* plan, medusa_dtype dt, int B, int H, int V) {
     if (!plan || !dtype_ok(dt) || B < 1 || H < 1 || V < 1) return 0;
-    return verify_layout(dt, B * plan->n_nodes, V).total;
+    return verify_layout(dt, B * plan->n_nodes, V, H).total;
 }
 
 medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt, int B, int H,
@@ -313,7 +313,7 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
     if (B < 1 || B > 4096 || H < 32 || H > 16384 || H % 32 != 0 || V < 1) return MEDUSA_ERR_SHAPE;
     if (!aligned16(node_hidden) || !aligned16(w_lm)) return MEDUSA_ERR_SHAPE;
     const int M = B * plan->n_nodes;
-    const VerifyLayout L = verify_layout(dt, M, V);
+    const VerifyLayout L = verify_layout(dt, M, V, H);
     if (!ws || ws_bytes < L.total) return MEDUSA_ERR_WORKSPACE;
     if (!plan->dev) return MEDUSA_ERR_PLAN_NOT_ON_DEVICE;
     medusa_status st = medusa_internal_device_check();
@@ -382,7 +382,7 @@ medusa_status medusa_proxy_qkv(medusa_dtype dt, int M, int H, int V, int Hq, int
         p.x_stride = H;
         p.N = Nn[i];
         p.tile_begin = tiles;
-        p.n_tiles = n_tiles_for(dt, M, EPI_STORE, Nn[i]);
+        p.n_tiles = n_tiles_for(dt, M, EPI_STORE, Nn[i], H);
         tiles += p.n_tiles;
         p.out = O[i];
         p.ldo = Nn[i];
@@ -414,7 +414,7 @@ medusa_status medusa_proxy_out(medusa_dtype dt, int M, int H, int V, int Hq, int
     p.x_stride = (long long)Hq * d;
     p.N = H;
     p.tile_begin = 0;
-    p.n_tiles = n_tiles_for(dt, M, EPI_STORE, H);
+    p.n_tiles = n_tiles_for(dt, M, EPI_STORE, H, Hq * d);
     p.out = node_hidden;
     p.ldo = H;
     p.res = embed;

@@ -200,6 +200,114 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_store_kernel(const GemmB
     store_epilogue<T, MT, RT>(P, bt, acc, m0, n_wave, ln, lg);
 }
 
+// Shared epilogue of the MFMA kernels: optional fp32 logits, then the per-tile argmax or
+// top-s of every input row.  acc[rt][mt][r] = Y[m0 + mt*16 + 4*lg + r][n_wave + rt*16 + ln];
+// `smem` must hold Mb * NWG floats (top-s only) and may alias the kernel's X staging area.
+template <int MT, int RT, int NWG, int EPI>
+__device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBatch& bt,
+                                              const floatx4 (&acc)[RT][MT], int m0, int Mb,
+                                              int tile, int n_wave, int wave, int lane,
+                                              unsigned char* smem, float (&red_v)[kWaves][MT * 16],
+                                              int (&red_i)[kWaves][MT * 16]) {
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int N = P.N;
+    if (P.logits) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int n = n_wave + rt * 16 + ln;
+            if (n >= N) continue;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + mt * 16 + 4 * lg + r;
+                    if (m < bt.M) P.logits[(long long)m * P.logits_ld + n] = acc[rt][mt][r];
+                }
+        }
+    }
+
+    if (EPI == EPI_ARGMAX) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float bv = -INFINITY;
+                int bi = INT_MAX;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const int n = n_wave + rt * 16 + ln;
+                    const float v = n < N ? acc[rt][mt][r] : -INFINITY;
+                    const int i = n < N ? n : INT_MAX;
+                    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+                }
+                reduce_best<16>(bv, bi);
+                if (ln == 0) {
+                    red_v[wave][mt * 16 + 4 * lg + r] = bv;
+                    red_i[wave][mt * 16 + 4 * lg + r] = bi;
+                }
+            }
+        __syncthreads();
+        for (int m = threadIdx.x; m < Mb; m += kThreads) {
+            float bv = red_v[0][m];
+            int bi = red_i[0][m];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+                if (better(red_v[w][m], red_i[w][m], bv, bi)) { bv = red_v[w][m]; bi = red_i[w][m]; }
+            const long long o = (long long)(m0 + m) * P.n_tiles + tile;
+            P.part_val[o] = bv;
+            P.part_idx[o] = bi;
+        }
+        return;
+    }
+
+    if (EPI == EPI_TOPS) {
+        // Only MT == 1 (<= 16 rows) is instantiated for this epilogue.
+        __syncthreads();
+        float* sv = reinterpret_cast<float*>(smem);      // [Mb][NWG]
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int nl = wave * RT * 16 + rt * 16 + ln;
+            const int n = tile * NWG + nl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * lg + r;
+                if (m < Mb) sv[m * NWG + nl] = n < N ? acc[rt][0][r] : -INFINITY;
+            }
+        }
+        __syncthreads();
+        constexpr int PER = NWG / kWave;
+        const int s = P.s;
+        for (int m = wave; m < Mb; m += kWaves) {
+            float v[PER];
+            int id[PER];
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int nl = lane + kWave * j;
+                const int n = tile * NWG + nl;
+                v[j] = n < N ? sv[m * NWG + nl] : -INFINITY;
+                id[j] = n < N ? n : INT_MAX;
+            }
+            const long long o = ((long long)(m0 + m) * P.n_tiles + tile) * s;
+            for (int round = 0; round < s; ++round) {
+                float bv = v[0];
+                int bi = id[0];
+#pragma unroll
+                for (int j = 1; j < PER; ++j)
+                    if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
+                reduce_best<kWave>(bv, bi);
+                if (lane == 0) {
+                    P.part_val[o + round] = bv;
+                    P.part_idx[o + round] = bi;
+                }
+#pragma unroll
+                for (int j = 0; j < PER; ++j)
+                    if (id[j] == bi) { v[j] = -INFINITY; id[j] = INT_MAX; }
+            }
+        }
+    }
+}
+
 template <typename T, int MT, int RT, int UN, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
     using E = Elem<T>;
@@ -334,100 +442,151 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
         return;
     }
 
-    if (P.logits) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int n = n_wave + rt * 16 + ln;
-            if (n >= N) continue;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + mt * 16 + 4 * lg + r;
-                    if (m < bt.M) P.logits[(long long)m * P.logits_ld + n] = acc[rt][mt][r];
-                }
-        }
-    }
+    tile_epilogue<MT, RT, NWG, EPI>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane, smem, red_v, red_i);
+}
 
-    if (EPI == EPI_ARGMAX) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float bv = -INFINITY;
-                int bi = INT_MAX;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const int n = n_wave + rt * 16 + ln;
-                    const float v = n < N ? acc[rt][mt][r] : -INFINITY;
-                    const int i = n < N ? n : INT_MAX;
-                    if (better(v, i, bv, bi)) { bv = v; bi = i; }
-                }
-                reduce_best<16>(bv, bi);
-                if (ln == 0) {
-                    red_v[wave][mt * 16 + 4 * lg + r] = bv;
-                    red_i[wave][mt * 16 + 4 * lg + r] = bi;
-                }
-            }
-        __syncthreads();
-        for (int m = threadIdx.x; m < Mb; m += kThreads) {
-            float bv = red_v[0][m];
-            int bi = red_i[0][m];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                if (better(red_v[w][m], red_i[w][m], bv, bi)) { bv = red_v[w][m]; bi = red_i[w][m]; }
-            const long long o = (long long)(m0 + m) * P.n_tiles + tile;
-            P.part_val[o] = bv;
-            P.part_idx[o] = bi;
-        }
-        return;
-    }
+// Row-streaming MFMA kernel (bf16; lm_head over the tree nodes, heads at batch > 2).
+// Each wave owns 16*RT weight rows and streams them in contraction chunks with
+// row-contiguous non-temporal loads (one instruction = 64 lanes x 16 contiguous bytes
+// spread over as many rows as the chunk requires), close to the access pattern that
+// reaches 7.0 TB/s.  The chunk is transposed through a wave-private
+// LDS tile into the MFMA operand layout (row l%16, k-slot 8*(l/16)); the X rows of the
+// chunk are staged once per workgroup and shared by the four waves.  The next chunk's
+// weights are in flight in registers while the current one is multiplied.
+// Chosen by a sweep at the 8B shape (lm_head over 64 nodes): chunk 64 / 4 tiles per wave
+// 161 us, 128 / 2: 172 us, 256 / 1: 236 us (the smaller chunk keeps LDS per workgroup low
+// enough for more workgroups per CU).
+#ifndef MEDUSA_RS_CHUNK
+#define MEDUSA_RS_CHUNK 64
+#endif
+#ifndef MEDUSA_RS_RTW
+#define MEDUSA_RS_RTW 4
+#endif
+constexpr int kRsChunk = MEDUSA_RS_CHUNK;   // contraction chunk per pass
+constexpr int kRsRtw = MEDUSA_RS_RTW;       // 16-row weight tiles per wave
 
-    if (EPI == EPI_TOPS) {
-        // Only MT == 1 (<= 16 rows) is instantiated for this epilogue.
-        __syncthreads();
-        float* sv = reinterpret_cast<float*>(smem);      // [Mb][NWG]
+template <int MT, int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatch bt) {
+    constexpr int RT = kRsRtw;
+    constexpr int ROWS = 16 * RT;             // weight rows per wave
+    constexpr int NWG = kWaves * ROWS;
+    constexpr int XP = kRsChunk + 8;          // LDS pitch of X rows and W tiles (elements)
+    constexpr int LPR = kRsChunk / 8;         // lanes per row in one load instruction
+    constexpr int RPI = kWave / LPR;          // rows per load instruction
+    constexpr int NI = ROWS / RPI;            // 16-byte loads per lane per chunk
+    __shared__ __align__(16) bf16_t xs[MT * 16 * XP];
+    __shared__ __align__(16) bf16_t wt[kWaves][ROWS * XP];
+    __shared__ float red_v[kWaves][MT * 16];
+    __shared__ int red_i[kWaves][MT * 16];
+
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    const int nblocks = bt.total_tiles * n_mb;
+    const int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int mb = bid % n_mb;
+    const int t = bid / n_mb;
+    const GemmProblem& P = bt.p[problem_of(bt, t)];
+    const int tile = t - P.tile_begin;
+    const int K = bt.K;
+    const int N = P.N;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int n_wave = tile * NWG + wave * ROWS;
+    const int m0 = mb * MT * 16;
+    const int Mb = min(bt.M - m0, MT * 16);
+
+    // load i covers rows RPI*i .. RPI*i+RPI-1 of the wave's rows, LPR lanes per row
+    const bf16_t* W = static_cast<const bf16_t*>(P.W);
+    const int half = lane / LPR;
+    const int col = (lane % LPR) * 8;
+    const u32x4* wsrc[NI];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int nl = wave * RT * 16 + rt * 16 + ln;
-            const int n = tile * NWG + nl;
+    for (int i = 0; i < NI; ++i) {
+        const int n = min(n_wave + RPI * i + half, N - 1);
+        wsrc[i] = reinterpret_cast<const u32x4*>(W + (long long)n * K + col);
+    }
+    u32x4 wr[NI];
+    auto load_w = [&](int kc) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 4 * lg + r;
-                if (m < Mb) sv[m * NWG + nl] = n < N ? acc[rt][0][r] : -INFINITY;
+        for (int i = 0; i < NI; ++i) wr[i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
+    };
+    const bf16_t* X = static_cast<const bf16_t*>(P.X);
+    bf16_t* wtile = wt[wave];
+
+    floatx4 acc[RT][MT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // X rows of the chunk are fetched one chunk ahead as well (XV vectors per thread)
+    constexpr int VPR = kRsChunk / 8;                       // 16-byte vectors per X row chunk
+    constexpr int XV = (MT * 16 * VPR + kThreads - 1) / kThreads;
+    const bf16_t* xrow_ptr[XV];
+    int xdst[XV];
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+        const int idx = threadIdx.x + j * kThreads;
+        const int m = idx / VPR;
+        const int c = idx - m * VPR;
+        xdst[j] = -1;
+        xrow_ptr[j] = nullptr;
+        if (m < Mb) {
+            long long r = m0 + m;
+            bool ok = true;
+            if (P.x_rows) {
+                r = P.x_rows[m0 + m];
+                ok = r >= 0 && r < bt.x_rows_bound;
             }
+            xdst[j] = m * XP + c * 8;
+            if (ok) xrow_ptr[j] = X + r * P.x_stride + c * 8;
         }
+    }
+    u32x4 xr[XV];
+    auto load_x = [&](int kc) {
+#pragma unroll
+        for (int j = 0; j < XV; ++j)
+            xr[j] = xrow_ptr[j] ? *reinterpret_cast<const u32x4*>(xrow_ptr[j] + kc)
+                                : u32x4{0u, 0u, 0u, 0u};
+    };
+
+    load_w(0);
+    load_x(0);
+    for (int kc = 0; kc < K; kc += kRsChunk) {
         __syncthreads();
-        constexpr int PER = NWG / kWave;
-        const int s = P.s;
-        for (int m = wave; m < Mb; m += kWaves) {
-            float v[PER];
-            int id[PER];
 #pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int nl = lane + kWave * j;
-                const int n = tile * NWG + nl;
-                v[j] = n < N ? sv[m * NWG + nl] : -INFINITY;
-                id[j] = n < N ? n : INT_MAX;
-            }
-            const long long o = ((long long)(m0 + m) * P.n_tiles + tile) * s;
-            for (int round = 0; round < s; ++round) {
-                float bv = v[0];
-                int bi = id[0];
+        for (int j = 0; j < XV; ++j)
+            if (xdst[j] >= 0) *reinterpret_cast<u32x4*>(xs + xdst[j]) = xr[j];
 #pragma unroll
-                for (int j = 1; j < PER; ++j)
-                    if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
-                reduce_best<kWave>(bv, bi);
-                if (lane == 0) {
-                    P.part_val[o + round] = bv;
-                    P.part_idx[o + round] = bi;
-                }
+        for (int i = 0; i < NI; ++i)
+            *reinterpret_cast<u32x4*>(wtile + (RPI * i + half) * XP + col) = wr[i];
+        __syncthreads();
+        if (kc + kRsChunk < K) {
+            load_w(kc + kRsChunk);
+            load_x(kc + kRsChunk);
+        }
 #pragma unroll
-                for (int j = 0; j < PER; ++j)
-                    if (id[j] == bi) { v[j] = -INFINITY; id[j] = INT_MAX; }
+        for (int ks = 0; ks < kRsChunk; ks += 32) {
+            Frag<bf16_t> wf[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) wf[rt].load(wtile + (rt * 16 + ln) * XP + ks + 8 * lg);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                Frag<bf16_t> xf;
+                const int m = mt * 16 + ln;
+                if (m < Mb) xf.load(xs + m * XP + ks + 8 * lg);
+                else xf.zero();
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) mma(acc[rt][mt], xf, wf[rt]);
             }
         }
     }
+    // the top-s epilogue needs Mb * NWG floats of scratch: the W tiles are free by now
+    static_assert(EPI != EPI_TOPS || sizeof(wt) >= 16 * NWG * sizeof(float), "top-s scratch");
+    __syncthreads();
+    tile_epilogue<MT, RT, NWG, EPI>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane,
+                                    reinterpret_cast<unsigned char*>(&wt[0][0]), red_v, red_i);
 }
 
 // GEMV for one or two input rows (the heads and the bootstrap root at batch 1): every
@@ -751,8 +910,11 @@ hipError_t launch_epi(int epi, GemmBatch& bt, hipStream_t stream) {
 
 }  // namespace
 
-int gemm_rows_per_tile(medusa_dtype dt, int M, int epi) {
+bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
+
+int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
+    if (rowstream_eligible(dt, epi, M, K)) return kWaves * 16 * kRsRtw;
     int rt;
     if (dt == MEDUSA_BF16)
         rt = epi == EPI_TOPS ? StreamCfg<bf16_t, EPI_TOPS>::RT : StreamCfg<bf16_t, EPI_ARGMAX>::RT;
@@ -798,7 +960,30 @@ bool gemv_eligible(medusa_dtype dt, int epi, const GemmBatch& bt) {
 
 }  // namespace
 
+template <int MT, int EPI>
+hipError_t launch_rowstream_t(GemmBatch& bt, hipStream_t stream) {
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    hipLaunchKernelGGL((gemm_rowstream_kernel<MT, EPI>), dim3(bt.total_tiles * n_mb),
+                       dim3(kThreads), 0, stream, bt);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
+    if (epi == EPI_TOPS) return launch_rowstream_t<1, EPI_TOPS>(bt, stream);
+    if (bt.M <= 16) return launch_rowstream_t<1, EPI_ARGMAX>(bt, stream);
+    if (bt.M <= 32) return launch_rowstream_t<2, EPI_ARGMAX>(bt, stream);
+    return launch_rowstream_t<4, EPI_ARGMAX>(bt, stream);
+}
+
+// Row-streaming MFMA path: bf16, contraction a multiple of its 256-wide chunk, argmax or
+// top-s epilogue (top-s only past the GEMV's two rows).
+bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K) {
+    if (dt != MEDUSA_BF16 || K % kRsChunk != 0) return false;
+    return epi == EPI_ARGMAX || (epi == EPI_TOPS && M > 2);
+}
+
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& bt, hipStream_t stream) {
+    if (rowstream_eligible(dt, epi, bt.M, bt.K)) return launch_rowstream(epi, bt, stream);
     if (gemv_eligible(dt, epi, bt))
         return epi == EPI_TOPS ? launch_gemv_k<EPI_TOPS>(bt, stream) : launch_gemv_k<EPI_STORE>(bt, stream);
     return dt == MEDUSA_BF16 ? launch_epi<bf16_t>(epi, bt, stream) : launch_epi<float>(epi, bt, stream);

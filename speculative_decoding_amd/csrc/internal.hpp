@@ -56,7 +56,7 @@ struct GemmBatch {
 };
 
 // Rows of W per workgroup for a given configuration.
-int gemm_rows_per_tile(medusa_dtype dt, int M, int epi);
+int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K);
 // Fills KC and launches.  Returns hipSuccess or the launch error.
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& batch, hipStream_t stream);
 
