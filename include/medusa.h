@@ -196,14 +196,18 @@ size_t medusa_verify_workspace(const medusa_tree_plan* plan, medusa_dtype dt, in
  *   proxy_qkv:  x_m = embed[tokens[m]]; q = rnd(Wq x) [M, Hq*d]; k = rnd(Wk x),
  *               v = rnd(Wv x) [M, Hkv*d].  Wq [Hq*d, H], Wk/Wv [Hkv*d, H].
  *   proxy_out:  node_hidden_m = rnd(embed[tokens[m]] + Wo o_m)  [M, H]; Wo [H, Hq*d],
- *               o [M, Hq*d].   H % 32 == 0 and (Hq*d) % 32 == 0. */
+ *               o [M, Hq*d].   H % 32 == 0 and (Hq*d) % 32 == 0.
+ * ws/ws_bytes: scratch for contraction-slice partial sums, at least
+ * medusa_proxy_workspace() bytes (the same buffer serves both calls). */
+size_t medusa_proxy_workspace(medusa_dtype dt, int M, int H, int Hq, int Hkv, int d);
 medusa_status medusa_proxy_qkv(medusa_dtype dt, int M, int H, int V, int Hq, int Hkv, int d,
                                const int32_t* tokens, const void* embed, const void* wq,
                                const void* wk, const void* wv, void* q, void* k, void* v,
-                               void* stream);
+                               void* ws, size_t ws_bytes, void* stream);
 medusa_status medusa_proxy_out(medusa_dtype dt, int M, int H, int V, int Hq, int d,
                                const int32_t* tokens, const void* embed, const void* o,
-                               const void* wo, void* node_hidden, void* stream);
+                               const void* wo, void* node_hidden, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* ------------------------------------------------------------------ misc */
 const char* medusa_status_string(medusa_status status);

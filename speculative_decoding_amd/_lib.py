@@ -47,11 +47,12 @@ _SIGS = {
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_size_t, c_void_p]),
     "medusa_verify_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int, c_int]),
+    "medusa_proxy_workspace": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "medusa_proxy_qkv": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                 c_void_p, c_void_p]),
+                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "medusa_proxy_out": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
-                                 c_void_p, c_void_p, c_void_p, c_void_p]),
+                                 c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "medusa_status_string": (c_char_p, [c_int]),
     "medusa_last_hip_error": (c_int, []),
     "medusa_version": (c_int, []),

@@ -352,10 +352,31 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
 
 // ------------------------------------------------------------------ one-layer verifier
 
+namespace {
+
+// Contraction slices for the verifier's two projections (0: direct store kernel).
+int qkv_ksplit(medusa_dtype dt, int M, int H, int Hq, int Hkv, int d) {
+    const int tiles = n_tiles_for(dt, M, EPI_PARTIAL, Hq * d, H) +
+                      2 * n_tiles_for(dt, M, EPI_PARTIAL, Hkv * d, H);
+    return store_ksplit(dt, M, H, tiles);
+}
+int out_ksplit(medusa_dtype dt, int M, int H, int Hq, int d) {
+    return store_ksplit(dt, M, Hq * d, n_tiles_for(dt, M, EPI_PARTIAL, H, Hq * d));
+}
+
+}  // namespace
+
+size_t medusa_proxy_workspace(medusa_dtype dt, int M, int H, int Hq, int Hkv, int d) {
+    if (!dtype_ok(dt) || M < 1 || H < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
+    const size_t a = (size_t)qkv_ksplit(dt, M, H, Hq, Hkv, d) * M * (size_t)(Hq * d + 2 * Hkv * d);
+    const size_t b = (size_t)out_ksplit(dt, M, H, Hq, d) * M * (size_t)H;
+    return align256((a > b ? a : b) * sizeof(float)) + 256;
+}
+
 medusa_status medusa_proxy_qkv(medusa_dtype dt, int M, int H, int V, int Hq, int Hkv, int d,
                                const int32_t* tokens, const void* embed, const void* wq,
                                const void* wk, const void* wv, void* q, void* k, void* v,
-                               void* stream) {
+                               void* ws, size_t ws_bytes, void* stream) {
     if (!tokens || !embed || !wq || !wk || !wv || !q || !k || !v) return MEDUSA_ERR_NULL;
     if (!dtype_ok(dt)) return MEDUSA_ERR_UNSUPPORTED;
     if (M < 1 || H < 32 || H > 16384 || H % 32 != 0 || V < 1 || Hq < 1 || Hkv < 1 || d < 1 ||
@@ -363,17 +384,22 @@ medusa_status medusa_proxy_qkv(medusa_dtype dt, int M, int H, int V, int Hq, int
         return MEDUSA_ERR_SHAPE;
     if (!aligned16(embed) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv))
         return MEDUSA_ERR_SHAPE;
+    const int ks = qkv_ksplit(dt, M, H, Hq, Hkv, d);
+    if (!ws || ws_bytes < medusa_proxy_workspace(dt, M, H, Hq, Hkv, d)) return MEDUSA_ERR_WORKSPACE;
     medusa_status st = medusa_internal_device_check();
     if (st != MEDUSA_OK) return st;
+    const int epi = ks > 0 ? EPI_PARTIAL : EPI_STORE;
     GemmBatch g{};
     g.n_problems = 3;
     g.M = M;
     g.K = H;
     g.x_rows_bound = V;
+    g.ksplit = ks > 0 ? ks : 1;
     const void* W[3] = {wq, wk, wv};
     void* O[3] = {q, k, v};
     const int Nn[3] = {Hq * d, Hkv * d, Hkv * d};
     int tiles = 0;
+    float* part = static_cast<float*>(ws);
     for (int i = 0; i < 3; ++i) {
         GemmProblem& p = g.p[i];
         p.W = W[i];
@@ -382,46 +408,63 @@ medusa_status medusa_proxy_qkv(medusa_dtype dt, int M, int H, int V, int Hq, int
         p.x_stride = H;
         p.N = Nn[i];
         p.tile_begin = tiles;
-        p.n_tiles = n_tiles_for(dt, M, EPI_STORE, Nn[i], H);
+        p.n_tiles = n_tiles_for(dt, M, epi, Nn[i], H);
         tiles += p.n_tiles;
         p.out = O[i];
         p.ldo = Nn[i];
+        p.part_val = part;
+        part += (size_t)g.ksplit * M * Nn[i];
     }
     g.total_tiles = tiles;
-    hipError_t e = timed_gemm("proxy_qkv", dt, EPI_STORE, g, static_cast<hipStream_t>(stream));
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    prof_begin("proxy_qkv", strm);
+    e = ks > 0 ? gemm_store_partial_launch(dt, g, strm) : gemm_launch(dt, EPI_STORE, g, strm);
+    prof_end(strm);
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     return MEDUSA_OK;
 }
 
 medusa_status medusa_proxy_out(medusa_dtype dt, int M, int H, int V, int Hq, int d,
                                const int32_t* tokens, const void* embed, const void* o,
-                               const void* wo, void* node_hidden, void* stream) {
+                               const void* wo, void* node_hidden, void* ws, size_t ws_bytes,
+                               void* stream) {
     if (!tokens || !embed || !o || !wo || !node_hidden) return MEDUSA_ERR_NULL;
     if (!dtype_ok(dt)) return MEDUSA_ERR_UNSUPPORTED;
     if (M < 1 || H < 16 || H % 16 != 0 || V < 1 || Hq < 1 || d < 1 || (Hq * d) % 32 != 0)
         return MEDUSA_ERR_SHAPE;
     if (!aligned16(embed) || !aligned16(o) || !aligned16(wo)) return MEDUSA_ERR_SHAPE;
+    const int ks = out_ksplit(dt, M, H, Hq, d);
+    const size_t need = align256((size_t)(ks > 0 ? ks : 0) * M * (size_t)H * sizeof(float)) + 256;
+    if (!ws || ws_bytes < need) return MEDUSA_ERR_WORKSPACE;
     medusa_status st = medusa_internal_device_check();
     if (st != MEDUSA_OK) return st;
+    const int epi = ks > 0 ? EPI_PARTIAL : EPI_STORE;
     GemmBatch g{};
     g.n_problems = 1;
     g.M = M;
     g.K = Hq * d;
     g.res_rows_bound = V;
+    g.ksplit = ks > 0 ? ks : 1;
     GemmProblem& p = g.p[0];
     p.W = wo;
     p.X = o;
     p.x_stride = (long long)Hq * d;
     p.N = H;
     p.tile_begin = 0;
-    p.n_tiles = n_tiles_for(dt, M, EPI_STORE, H, Hq * d);
+    p.n_tiles = n_tiles_for(dt, M, epi, H, Hq * d);
     p.out = node_hidden;
     p.ldo = H;
     p.res = embed;
     p.res_rows = tokens;
     p.res_stride = H;
+    p.part_val = static_cast<float*>(ws);
     g.total_tiles = p.n_tiles;
-    hipError_t e = timed_gemm("proxy_out", dt, EPI_STORE, g, static_cast<hipStream_t>(stream));
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    prof_begin("proxy_out", strm);
+    e = ks > 0 ? gemm_store_partial_launch(dt, g, strm) : gemm_launch(dt, EPI_STORE, g, strm);
+    prof_end(strm);
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     return MEDUSA_OK;
 }

@@ -463,11 +463,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
 #define MEDUSA_RS_RTW 4
 #endif
 constexpr int kRsChunk = MEDUSA_RS_CHUNK;   // contraction chunk per pass
-constexpr int kRsRtw = MEDUSA_RS_RTW;       // 16-row weight tiles per wave
+constexpr int kRsRtw = MEDUSA_RS_RTW;       // 16-row weight tiles per wave (argmax, top-s)
+constexpr int kRsRtwPartial = 1;            // ... for contraction slices (small weights)
 
-template <int MT, int EPI>
+template <int MT, int EPI, int RTW>
 __global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatch bt) {
-    constexpr int RT = kRsRtw;
+    constexpr int RT = RTW;
     constexpr int ROWS = 16 * RT;             // weight rows per wave
     constexpr int NWG = kWaves * ROWS;
     constexpr int XP = kRsChunk + 8;          // LDS pitch of X rows and W tiles (elements)
@@ -480,14 +481,22 @@ __global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatc
     __shared__ int red_i[kWaves][MT * 16];
 
     const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
-    const int nblocks = bt.total_tiles * n_mb;
-    const int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int nks = EPI == EPI_PARTIAL ? bt.ksplit : 1;
+    const int nblocks = bt.total_tiles * n_mb * nks;
+    int bid = xcd_logical_block(blockIdx.x, nblocks);
     const int mb = bid % n_mb;
-    const int t = bid / n_mb;
+    bid /= n_mb;
+    const int ksl = bid % nks;
+    const int t = bid / nks;
     const GemmProblem& P = bt.p[problem_of(bt, t)];
     const int tile = t - P.tile_begin;
     const int K = bt.K;
     const int N = P.N;
+    // contraction slice of this block (whole chunks)
+    const int chunks = K / kRsChunk;
+    const int per = (chunks + nks - 1) / nks;
+    const int k_lo = min(K, ksl * per * kRsChunk);
+    const int k_hi = min(K, (ksl + 1) * per * kRsChunk);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int ln = lane & 15;
@@ -551,9 +560,11 @@ __global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatc
                                 : u32x4{0u, 0u, 0u, 0u};
     };
 
-    load_w(0);
-    load_x(0);
-    for (int kc = 0; kc < K; kc += kRsChunk) {
+    if (k_lo < k_hi) {
+        load_w(k_lo);
+        load_x(k_lo);
+    }
+    for (int kc = k_lo; kc < k_hi; kc += kRsChunk) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < XV; ++j)
@@ -562,7 +573,7 @@ __global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatc
         for (int i = 0; i < NI; ++i)
             *reinterpret_cast<u32x4*>(wtile + (RPI * i + half) * XP + col) = wr[i];
         __syncthreads();
-        if (kc + kRsChunk < K) {
+        if (kc + kRsChunk < k_hi) {
             load_w(kc + kRsChunk);
             load_x(kc + kRsChunk);
         }
@@ -582,11 +593,72 @@ __global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatc
             }
         }
     }
+    if (EPI == EPI_PARTIAL) {
+        float* part = P.part_val + (long long)ksl * bt.M * N;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int n = n_wave + rt * 16 + ln;
+            if (n >= N) continue;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + mt * 16 + 4 * lg + r;
+                    if (m < bt.M) part[(long long)m * N + n] = acc[rt][mt][r];
+                }
+        }
+        return;
+    }
     // the top-s epilogue needs Mb * NWG floats of scratch: the W tiles are free by now
     static_assert(EPI != EPI_TOPS || sizeof(wt) >= 16 * NWG * sizeof(float), "top-s scratch");
     __syncthreads();
     tile_epilogue<MT, RT, NWG, EPI>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane,
                                     reinterpret_cast<unsigned char*>(&wt[0][0]), red_v, red_i);
+}
+
+// Sum the contraction slices of every (m, n) in slice order and apply the store epilogue:
+// out[m][n] = rnd(silu?(sum + bias[n]) + residual[m][n]).  Four consecutive n per thread.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void splitk_finalize_kernel(const GemmBatch bt) {
+    using E = Elem<T>;
+    long long q = (long long)blockIdx.x * kThreads + threadIdx.x;     // quad index
+    int pi = 0;
+    for (; pi < bt.n_problems; ++pi) {
+        const long long nq = (long long)bt.M * ((bt.p[pi].N + 3) / 4);
+        if (q < nq) break;
+        q -= nq;
+    }
+    if (pi >= bt.n_problems) return;
+    const GemmProblem& P = bt.p[pi];
+    const int N = P.N;
+    const int qpr = (N + 3) / 4;
+    const int m = (int)(q / qpr);
+    const int n0 = (int)(q - (long long)m * qpr) * 4;
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < bt.ksplit; ++ks) {
+        const float* part = P.part_val + ((long long)ks * bt.M + m) * N;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (n0 + j < N) y[j] += part[n0 + j];
+    }
+    const T* bias = static_cast<const T*>(P.bias);
+    const T* res = static_cast<const T*>(P.res);
+    long long rr = m;
+    bool rok = res != nullptr;
+    if (rok && P.res_rows) {
+        rr = P.res_rows[m];
+        rok = rr >= 0 && rr < bt.res_rows_bound;
+    }
+    T* out = static_cast<T*>(P.out);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + j;
+        if (n >= N) continue;
+        float v = y[j] + (bias ? E::to_f32(bias[n]) : 0.f);
+        if (P.silu) v = silu(v);
+        if (rok) v += E::to_f32(res[rr * P.res_stride + n]);
+        out[(long long)m * P.ldo + n] = E::from_f32(v);
+    }
 }
 
 // GEMV for one or two input rows (the heads and the bootstrap root at batch 1): every
@@ -914,6 +986,7 @@ bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
 
 int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
+    if (epi == EPI_PARTIAL) return kWaves * 16 * kRsRtwPartial;
     if (rowstream_eligible(dt, epi, M, K)) return kWaves * 16 * kRsRtw;
     int rt;
     if (dt == MEDUSA_BF16)
@@ -960,19 +1033,25 @@ bool gemv_eligible(medusa_dtype dt, int epi, const GemmBatch& bt) {
 
 }  // namespace
 
-template <int MT, int EPI>
+template <int MT, int EPI, int RTW>
 hipError_t launch_rowstream_t(GemmBatch& bt, hipStream_t stream) {
     const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
-    hipLaunchKernelGGL((gemm_rowstream_kernel<MT, EPI>), dim3(bt.total_tiles * n_mb),
+    const int nks = EPI == EPI_PARTIAL ? bt.ksplit : 1;
+    hipLaunchKernelGGL((gemm_rowstream_kernel<MT, EPI, RTW>), dim3(bt.total_tiles * n_mb * nks),
                        dim3(kThreads), 0, stream, bt);
     return hipGetLastError();
 }
 
 hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
-    if (epi == EPI_TOPS) return launch_rowstream_t<1, EPI_TOPS>(bt, stream);
-    if (bt.M <= 16) return launch_rowstream_t<1, EPI_ARGMAX>(bt, stream);
-    if (bt.M <= 32) return launch_rowstream_t<2, EPI_ARGMAX>(bt, stream);
-    return launch_rowstream_t<4, EPI_ARGMAX>(bt, stream);
+    if (epi == EPI_TOPS) return launch_rowstream_t<1, EPI_TOPS, kRsRtw>(bt, stream);
+    if (epi == EPI_PARTIAL) {
+        if (bt.M <= 16) return launch_rowstream_t<1, EPI_PARTIAL, kRsRtwPartial>(bt, stream);
+        if (bt.M <= 32) return launch_rowstream_t<2, EPI_PARTIAL, kRsRtwPartial>(bt, stream);
+        return launch_rowstream_t<4, EPI_PARTIAL, kRsRtwPartial>(bt, stream);
+    }
+    if (bt.M <= 16) return launch_rowstream_t<1, EPI_ARGMAX, kRsRtw>(bt, stream);
+    if (bt.M <= 32) return launch_rowstream_t<2, EPI_ARGMAX, kRsRtw>(bt, stream);
+    return launch_rowstream_t<4, EPI_ARGMAX, kRsRtw>(bt, stream);
 }
 
 // Row-streaming MFMA path: bf16, contraction a multiple of its 256-wide chunk, argmax or
@@ -980,6 +1059,26 @@ hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
 bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K) {
     if (dt != MEDUSA_BF16 || K % kRsChunk != 0) return false;
     return epi == EPI_ARGMAX || (epi == EPI_TOPS && M > 2);
+}
+
+int store_ksplit(medusa_dtype dt, int M, int K, int tiles) {
+    if (dt != MEDUSA_BF16 || M <= 16 || K % kRsChunk != 0) return 0;
+    const int n_mb = (M + 63) / 64;
+    const int want = (384 + tiles * n_mb - 1) / (tiles * n_mb);   // about 384 workgroups
+    return max(1, min(want, min(8, K / kRsChunk)));
+}
+
+hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& bt, hipStream_t stream) {
+    hipError_t e = launch_rowstream(EPI_PARTIAL, bt, stream);
+    if (e != hipSuccess) return e;
+    long long quads = 0;
+    for (int p = 0; p < bt.n_problems; ++p) quads += (long long)bt.M * ((bt.p[p].N + 3) / 4);
+    const int blocks = (int)((quads + kThreads - 1) / kThreads);
+    if (dt == MEDUSA_BF16)
+        hipLaunchKernelGGL(splitk_finalize_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, stream, bt);
+    else
+        hipLaunchKernelGGL(splitk_finalize_kernel<float>, dim3(blocks), dim3(kThreads), 0, stream, bt);
+    return hipGetLastError();
 }
 
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& bt, hipStream_t stream) {

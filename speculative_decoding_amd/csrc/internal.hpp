@@ -18,6 +18,7 @@ enum Epilogue : int {
     EPI_STORE = 0,   // out[m*ldo + n] = rnd(silu?(acc + bias[n]) + residual[m][n])
     EPI_TOPS = 1,    // per row m: the tile's top-s (value desc, id asc) -> partials
     EPI_ARGMAX = 2,  // per row m: the tile's best (value, id) -> partials
+    EPI_PARTIAL = 3, // fp32 partial sums of one contraction slice -> part_val[slice][m][n]
 };
 
 struct GemmProblem {
@@ -53,12 +54,21 @@ struct GemmBatch {
     int KC;                   // contraction chunk staged in LDS per pass
     int x_rows_bound;
     int res_rows_bound;
+    int ksplit;               // contraction slices (EPI_PARTIAL); 1 otherwise
 };
 
 // Rows of W per workgroup for a given configuration.
 int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K);
 // Fills KC and launches.  Returns hipSuccess or the launch error.
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& batch, hipStream_t stream);
+
+// Store GEMMs with many input rows (the verifier's projections) run as contraction slices
+// on the row-streaming kernel (EPI_PARTIAL) plus a finalize pass that sums the slices in
+// order and applies the store epilogue.  store_ksplit() > 0 selects that path; it returns
+// the number of slices for `tiles` weight tiles (rows per tile from gemm_rows_per_tile
+// with EPI_PARTIAL).  The caller points each problem's part_val at ksplit*M*N floats.
+int store_ksplit(medusa_dtype dt, int M, int K, int tiles);
+hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& batch, hipStream_t stream);
 
 // ------------------------------------------------------------------ top-s merge
 struct MergeProblem {

@@ -234,22 +234,29 @@ def medusa_verify_accept(plan: TreePlan, dt, B, H, V, node_hidden, w_lm, node_to
     _check("medusa_verify_accept", st)
 
 
-def medusa_proxy_qkv(dt, M, H, V, Hq, Hkv, d, tokens, embed, wq, wk, wv, q, k, v, stream=None):
+def medusa_proxy_workspace(dt, M, H, Hq, Hkv, d) -> int:
+    return int(lib().medusa_proxy_workspace(_dt(dt), M, H, Hq, Hkv, d))
+
+
+def medusa_proxy_qkv(dt, M, H, V, Hq, Hkv, d, tokens, embed, wq, wk, wv, q, k, v, ws,
+                     stream=None):
     torch = _torch()
     st = lib().medusa_proxy_qkv(
         _dt(dt), M, H, V, Hq, Hkv, d, _ptr(tokens, torch.int32, "tokens"),
         _float_ptr(embed, dt, "embed"), _float_ptr(wq, dt, "wq"), _float_ptr(wk, dt, "wk"),
         _float_ptr(wv, dt, "wv"), _float_ptr(q, dt, "q"), _float_ptr(k, dt, "k"),
-        _float_ptr(v, dt, "v"), _stream(stream))
+        _float_ptr(v, dt, "v"), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check("medusa_proxy_qkv", st)
 
 
-def medusa_proxy_out(dt, M, H, V, Hq, d, tokens, embed, o, wo, node_hidden, stream=None):
+def medusa_proxy_out(dt, M, H, V, Hq, d, tokens, embed, o, wo, node_hidden, ws, stream=None):
     torch = _torch()
     st = lib().medusa_proxy_out(
         _dt(dt), M, H, V, Hq, d, _ptr(tokens, torch.int32, "tokens"),
         _float_ptr(embed, dt, "embed"), _float_ptr(o, dt, "o"), _float_ptr(wo, dt, "wo"),
-        _float_ptr(node_hidden, dt, "node_hidden"), _stream(stream))
+        _float_ptr(node_hidden, dt, "node_hidden"), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check("medusa_proxy_out", st)
 
 

@@ -95,6 +95,8 @@ class MedusaStep:
         self.ws_attn = torch.empty(M.medusa_attention_workspace(plan, dims.dtype, B, dims.Hq,
                                                                 dims.Hkv, dims.d, dims.Lcap), **u8)
         self.ws_verify = torch.empty(M.medusa_verify_workspace(plan, dims.dtype, B, H, V), **u8)
+        self.ws_proxy = torch.empty(M.medusa_proxy_workspace(dims.dtype, B * n, H, dims.Hq,
+                                                             dims.Hkv, dims.d), **u8)
 
     # ---- the four calls plus the verifier layer, in step order
     def heads(self, bootstrap_root: bool = False, keep_u: bool = True):
@@ -112,7 +114,8 @@ class MedusaStep:
     def verifier_in(self):
         d, w = self.dims, self.w
         M.medusa_proxy_qkv(d.dtype, d.B * self.N, d.H, d.V, d.Hq, d.Hkv, d.d, self.node_tokens,
-                           w["embed"], w["wq"], w["wk"], w["wv"], self.q, self.k_tree, self.v_tree)
+                           w["embed"], w["wq"], w["wk"], w["wv"], self.q, self.k_tree, self.v_tree,
+                           self.ws_proxy)
 
     def attention(self):
         d, w = self.dims, self.w
@@ -123,7 +126,7 @@ class MedusaStep:
     def verifier_out(self):
         d, w = self.dims, self.w
         M.medusa_proxy_out(d.dtype, d.B * self.N, d.H, d.V, d.Hq, d.d, self.node_tokens,
-                           w["embed"], self.o, w["wo"], self.node_hidden)
+                           w["embed"], self.o, w["wo"], self.node_hidden, self.ws_proxy)
 
     def verify(self):
         d, w = self.dims, self.w

@@ -145,6 +145,10 @@ def test_tree_and_attention_error_paths():
     assert L.medusa_verify_accept(plan.handle, 1, 1, 4095, 1000, FAKE, FAKE, FAKE, None, FAKE,
                                   FAKE, FAKE, None, FAKE, 1 << 40, None) == 2
     assert L.medusa_proxy_qkv(1, 9, 256, 1000, 4, 4, 64, None, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE, FAKE, None) == 1
-    assert L.medusa_proxy_out(1, 9, 250, 1000, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+                              FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    assert L.medusa_proxy_out(1, 9, 250, 1000, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                              None) == 2
+    assert L.medusa_proxy_qkv(1, 64, 4096, 1000, 32, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, FAKE, 64, None) == 5
+    assert M.medusa_proxy_workspace("bf16", 64, 4096, 32, 8, 128) > 1 << 20
     assert L.medusa_status_string(5) == b"workspace too small"
