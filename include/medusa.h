@@ -223,6 +223,9 @@ int medusa_version(void);
  * "verify_lmhead", "verify_accept").  Not thread-safe; at most 8192 launches are
  * recorded between resets (later ones are not timed). */
 medusa_status medusa_profile_enable(int on);
+/* Restrict timing to the launches of one kernel (NULL: time every kernel).  Each timed
+ * launch adds two event records to its stream, which costs a few microseconds. */
+medusa_status medusa_profile_only(const char* kernel);
 medusa_status medusa_profile_reset(void);
 medusa_status medusa_profile_query(const char* kernel, double* total_ms, int* launches);
 

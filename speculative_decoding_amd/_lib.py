@@ -58,6 +58,7 @@ _SIGS = {
     "medusa_version": (c_int, []),
     "medusa_profile_enable": (c_int, [c_int]),
     "medusa_profile_reset": (c_int, []),
+    "medusa_profile_only": (c_int, [c_char_p]),
     "medusa_profile_query": (c_int, [c_char_p, P_f64, ctypes.POINTER(c_int)]),
 }
 

@@ -150,18 +150,24 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
     constexpr int VPR = D / EPV;                 // 16-byte vectors per key row
     constexpr int NV = kKeys * VPR / kThreads;   // vectors per thread per block
     u32x4 kr[NV], vr[NV];
+    // K: consecutive threads read consecutive 16-byte pieces of a key row (coalesced, and
+    // stored row-major).  V: consecutive threads take consecutive keys of one 16-byte column
+    // piece, so the transposed scalar LDS stores of a wave hit 64 consecutive keys of one
+    // V^T row (no bank conflicts) instead of 16 rows that all map to the same bank.
     auto fetch = [&](int kb0) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int idx = threadIdx.x + j * kThreads;
             const int key = idx / VPR;
             const int c = idx - key * VPR;
+            const int vkey = idx % kKeys;
+            const int vc = idx / kKeys;
             kr[j] = u32x4{0u, 0u, 0u, 0u};
             vr[j] = kr[j];
-            if (kb0 + key < k_end) {
+            if (kb0 + key < k_end)
                 kr[j] = *reinterpret_cast<const u32x4*>(ksrc + (long long)(kb0 + key) * kstride + c * EPV);
-                vr[j] = *reinterpret_cast<const u32x4*>(vsrc + (long long)(kb0 + key) * kstride + c * EPV);
-            }
+            if (kb0 + vkey < k_end)
+                vr[j] = *reinterpret_cast<const u32x4*>(vsrc + (long long)(kb0 + vkey) * kstride + vc * EPV);
         }
     };
     fetch(k_begin);
@@ -173,8 +179,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
             const int key = idx / VPR;
             const int c = idx - key * VPR;
             *reinterpret_cast<u32x4*>(Ks + key * KP + c * EPV) = kr[j];
+            const int vkey = idx % kKeys;
+            const int vc = idx / kKeys;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) Vt[(c * EPV + e) * VP + key] = Vt4<T>::elem(vr[j], e);
+            for (int e = 0; e < EPV; ++e) Vt[(vc * EPV + e) * VP + vkey] = Vt4<T>::elem(vr[j], e);
         }
         __syncthreads();
         if (kb0 + kKeys < k_end) fetch(kb0 + kKeys);

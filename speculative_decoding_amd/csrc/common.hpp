@@ -93,6 +93,69 @@ __device__ __forceinline__ void reduce_best(float& v, int& i) {
     }
 }
 
+// ---------------------------------------------------------------- DPP reductions
+// Within a row of 16 lanes: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane i <- 7-i within 8) and row_mirror (lane i <- 15-i within 16) pair
+// every lane with one from the other half at each step, so four steps reduce a row; the
+// four row results are then read with readlane.  DPP moves stay in the VALU (no LDS
+// crossbar round trip), and the order of the additions / comparisons is fixed.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+    const float ov = dpp_f<CTRL>(v);
+    const int oi = dpp_i<CTRL>(i);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Best (value, id) over each row of 16 lanes; every lane of the row gets it.
+__device__ __forceinline__ void row_best(float& v, int& i) {
+    best_step<kDppXor1>(v, i);
+    best_step<kDppXor2>(v, i);
+    best_step<kDppHalfMirror>(v, i);
+    best_step<kDppMirror>(v, i);
+}
+
+// Best (value, id) over the whole wave; every lane gets it.
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+    row_best(v, i);
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+        if (better(rv, ri, bv, bi)) { bv = rv; bi = ri; }
+    }
+    v = bv;
+    i = bi;
+}
+
+// Sum over the whole wave in a fixed order; every lane gets it.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (a + b) + (c + d);
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 // Blocks are dispatched round robin over the 8 XCDs (block i on XCD i % 8).  Map the

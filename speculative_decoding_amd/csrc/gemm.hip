@@ -241,7 +241,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBa
                     const int i = n < N ? n : INT_MAX;
                     if (better(v, i, bv, bi)) { bv = v; bi = i; }
                 }
-                reduce_best<16>(bv, bi);
+                row_best(bv, bi);
                 if (ln == 0) {
                     red_v[wave][mt * 16 + 4 * lg + r] = bv;
                     red_i[wave][mt * 16 + 4 * lg + r] = bi;
@@ -295,7 +295,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBa
 #pragma unroll
                 for (int j = 1; j < PER; ++j)
                     if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
-                reduce_best<kWave>(bv, bi);
+                wave_best(bv, bi);
                 if (lane == 0) {
                     P.part_val[o + round] = bv;
                     P.part_idx[o + round] = bi;
@@ -686,12 +686,6 @@ __device__ __forceinline__ float dot8(const u32x4& w, const u32x4& x, float acc)
     return acc;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
-    return v;
-}
-
 template <int NCH, int MV, int R, int EPI>
 __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemmBatch bt) {
     constexpr int RPW = EPI == EPI_TOPS ? 32 : 8;      // weight rows per wave
@@ -746,7 +740,7 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemmBatch bt)
                 float acc = 0.f;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) acc = dot8(w[r][c], xs[mv][c], acc);
-                acc = wave_sum(acc);
+                acc = wave_sum_dpp(acc);
                 if (lane == 0) yl[mv][wave * RPW + j + r] = acc;
             }
     };
@@ -817,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemmBatch bt)
 #pragma unroll
             for (int j = 1; j < PER; ++j)
                 if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
-            reduce_best<kWave>(bv, bi);
+            wave_best(bv, bi);
             if (lane == 0) {
                 P.part_val[o + round] = bv;
                 P.part_idx[o + round] = bi;
@@ -829,95 +823,110 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemmBatch bt)
     }
 }
 
-// k-way merge of the per-tile candidate lists (each sorted best first) into the top-s.
-// The lists are first copied to LDS when they fit, so each round costs one block-wide
-// reduction; the wave winners alternate between two LDS slots so one barrier per round
-// suffices.
-constexpr int kMergeLdsEntries = 12288;  // 96 KB of (value, id) pairs
+// Merge of the per-tile candidate lists (each sorted best first) into the top-s.
+// Pruning: a candidate of tile t can only be in the global top-s if t is among the s tiles
+// whose best candidates rank highest (otherwise s better candidates exist, one per better
+// tile).  So the merge reads every tile's first entry, picks those s tiles, and selects the
+// top-s among their s*s entries: about n_tiles + s*s loads instead of n_tiles*s.  Both
+// selections run in one wave with wave-wide (value desc, id asc) reductions.
+constexpr int kMergeMaxTiles = 2048;
+constexpr int kMergeMaxCand = MEDUSA_MAX_TOPK * MEDUSA_MAX_TOPK;
 
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch bt) {
-    extern __shared__ __align__(16) unsigned char msmem[];
-    float* lv = reinterpret_cast<float*>(msmem);
-    int* li = reinterpret_cast<int*>(lv + kMergeLdsEntries);
-    __shared__ float sv[2][kWaves];
-    __shared__ int si[2][kWaves];
-    constexpr int kMaxOwned = 8;
+    __shared__ float tv[kMergeMaxTiles];
+    __shared__ int ti[kMergeMaxTiles];
+    __shared__ int best_tiles[MEDUSA_MAX_TOPK];
+    __shared__ float cv[kMergeMaxCand];
+    __shared__ int ci[kMergeMaxCand];
     const int p = blockIdx.x / bt.M;
     const int m = blockIdx.x - p * bt.M;
     const MergeProblem& P = bt.p[p];
     const int s = P.s;
-    const float* pv = P.part_val + (long long)m * P.n_tiles * s;
-    const int32_t* pi = P.part_idx + (long long)m * P.n_tiles * s;
+    const int nt = P.n_tiles;
+    const float* pv = P.part_val + (long long)m * nt * s;
+    const int32_t* pi = P.part_idx + (long long)m * nt * s;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int total = P.n_tiles * s;
-    const bool in_lds = total <= kMergeLdsEntries;
-    if (in_lds) {
-        // eight independent loads per thread in flight before the LDS stores
-        for (int base = threadIdx.x; base < total; base += 8 * kThreads) {
-            float v[8];
-            int id[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int i = base + j * kThreads;
-                v[j] = i < total ? pv[i] : 0.f;
-                id[j] = i < total ? pi[i] : 0;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int i = base + j * kThreads;
-                if (i < total) { lv[i] = v[j]; li[i] = id[j]; }
-            }
-        }
-        __syncthreads();
-    }
-    auto fetch = [&](int idx, float& v, int& id) {
-        if (in_lds) { v = lv[idx]; id = li[idx]; }
-        else { v = pv[idx]; id = pi[idx]; }
-    };
 
-    int ptr[kMaxOwned];
-    float hv[kMaxOwned];
-    int hi[kMaxOwned];
+    // 1. every tile's best entry into LDS (tile index kept implicitly by position)
+    for (int t0 = threadIdx.x; t0 < nt; t0 += 8 * kThreads) {
+        float v[8];
+        int id[8];
 #pragma unroll
-    for (int j = 0; j < kMaxOwned; ++j) {
-        const int tl = threadIdx.x + j * kThreads;
-        ptr[j] = 0;
-        hv[j] = -INFINITY;
-        hi[j] = INT_MAX;
-        if (tl < P.n_tiles) fetch(tl * s, hv[j], hi[j]);
-    }
-    for (int round = 0; round < s; ++round) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-#pragma unroll
-        for (int j = 0; j < kMaxOwned; ++j)
-            if (better(hv[j], hi[j], bv, bi)) { bv = hv[j]; bi = hi[j]; }
-        const int mine = bi;
-        reduce_best<kWave>(bv, bi);
-        const int slot = round & 1;
-        if (lane == 0) { sv[slot][wave] = bv; si[slot][wave] = bi; }
-        __syncthreads();
-        bv = sv[slot][0];
-        bi = si[slot][0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-            if (better(sv[slot][w], si[slot][w], bv, bi)) { bv = sv[slot][w]; bi = si[slot][w]; }
-        if (threadIdx.x == 0) {
-            P.out_ids[(long long)m * P.out_ld + round] = bi == INT_MAX ? -1 : bi;
-            if (P.out_vals) P.out_vals[(long long)m * P.out_ld + round] = bv;
+        for (int j = 0; j < 8; ++j) {
+            const int t = t0 + j * kThreads;
+            v[j] = t < nt ? pv[(long long)t * s] : -INFINITY;
+            id[j] = t < nt ? pi[(long long)t * s] : INT_MAX;
         }
-        if (mine == bi && bi != INT_MAX) {
 #pragma unroll
-            for (int j = 0; j < kMaxOwned; ++j) {
-                if (hi[j] == bi) {
-                    const int tl = threadIdx.x + j * kThreads;
-                    ++ptr[j];
-                    hv[j] = -INFINITY;
-                    hi[j] = INT_MAX;
-                    if (ptr[j] < s) fetch(tl * s + ptr[j], hv[j], hi[j]);
+        for (int j = 0; j < 8; ++j) {
+            const int t = t0 + j * kThreads;
+            if (t < nt) { tv[t] = v[j]; ti[t] = id[j]; }
+        }
+    }
+    __syncthreads();
+    // 2. wave 0: the s tiles with the best first entries (each lane keeps its share of the
+    //    tile maxima in registers; tile t sits in lane t % 64, slot t / 64)
+    if (wave == 0) {
+        constexpr int kSlots = kMergeMaxTiles / kWave;
+        float rv_[kSlots];
+        int ri_[kSlots];
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j) {
+            const int t = lane + kWave * j;
+            rv_[j] = t < nt ? tv[t] : -INFINITY;
+            ri_[j] = t < nt ? ti[t] : INT_MAX;
+        }
+        for (int round = 0; round < s; ++round) {
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+#pragma unroll
+            for (int j = 0; j < kSlots; ++j)
+                if (better(rv_[j], ri_[j], bv, bi)) { bv = rv_[j]; bi = ri_[j]; }
+            wave_best(bv, bi);
+            int owner_t = -1;
+#pragma unroll
+            for (int j = 0; j < kSlots; ++j)
+                if (ri_[j] == bi && bi != INT_MAX) {
+                    owner_t = lane + kWave * j;
+                    rv_[j] = -INFINITY;
+                    ri_[j] = INT_MAX;
                 }
+            if (owner_t >= 0) best_tiles[round] = owner_t;
+            if (bi == INT_MAX && lane == 0) best_tiles[round] = -1;
+        }
+    }
+    __syncthreads();
+    // 3. their lists into LDS
+    const int nc = s * s;
+    for (int c = threadIdx.x; c < nc; c += kThreads) {
+        const int r = c / s;
+        const int j = c - r * s;
+        const int t = best_tiles[r];
+        cv[c] = t >= 0 ? pv[(long long)t * s + j] : -INFINITY;
+        ci[c] = t >= 0 ? pi[(long long)t * s + j] : INT_MAX;
+    }
+    __syncthreads();
+    // 4. wave 0: the top-s of those candidates, in order
+    if (wave == 0) {
+        for (int round = 0; round < s; ++round) {
+            float bv = -INFINITY;
+            int bi = INT_MAX, bc = -1;
+            for (int c = lane; c < nc; c += kWave)
+                if (better(cv[c], ci[c], bv, bi)) { bv = cv[c]; bi = ci[c]; bc = c; }
+            float rv = bv;
+            int ri = bi;
+            wave_best(rv, ri);
+            if (lane == 0) {
+                P.out_ids[(long long)m * P.out_ld + round] = ri == INT_MAX ? -1 : ri;
+                if (P.out_vals) P.out_vals[(long long)m * P.out_ld + round] = rv;
             }
+            if (ri == bi && bc >= 0 && ri != INT_MAX) {
+                cv[bc] = -INFINITY;
+                ci[bc] = INT_MAX;
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         }
     }
     for (int r = s + threadIdx.x; r < P.s_pad; r += kThreads) {
@@ -1089,8 +1098,9 @@ hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& bt, hipStream_t stre
 }
 
 hipError_t topk_merge_launch(const MergeBatch& bt, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(bt.n_problems * bt.M), dim3(kThreads),
-                       kMergeLdsEntries * (sizeof(float) + sizeof(int)), stream, bt);
+    for (int p = 0; p < bt.n_problems; ++p)
+        if (bt.p[p].n_tiles > kMergeMaxTiles || bt.p[p].s > MEDUSA_MAX_TOPK) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(bt.n_problems * bt.M), dim3(kThreads), 0, stream, bt);
     return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <string>
 #include <vector>
 
 #include "plan_impl.hpp"
@@ -17,6 +18,7 @@ struct Record {
 };
 
 bool g_on = false;
+std::string g_only;                 // when non-empty, only this kernel is timed
 std::vector<hipEvent_t> g_events;   // 2 per record slot, created on enable
 std::vector<Record> g_records;
 int g_open = -1;
@@ -26,7 +28,9 @@ int g_open = -1;
 namespace medusa {
 
 void prof_begin(const char* name, hipStream_t stream) {
+    g_open = -1;
     if (!g_on) return;
+    if (!g_only.empty() && g_only != name) return;
     const int slot = (int)g_records.size();
     if (slot >= kMaxRecords || 2 * slot + 1 >= (int)g_events.size()) {
         g_open = -1;
@@ -67,6 +71,11 @@ medusa_status medusa_profile_enable(int on) {
         }
     }
     g_on = on != 0;
+    return MEDUSA_OK;
+}
+
+medusa_status medusa_profile_only(const char* kernel) {
+    g_only = kernel ? kernel : "";
     return MEDUSA_OK;
 }
 

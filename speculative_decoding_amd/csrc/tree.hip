@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
                     if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
             }
         }
-        reduce_best<kPerNode>(bv, bi);
+        row_best(bv, bi);     // the 16 lanes of a node form one DPP row
         if (sub == 0 && i < N) {
             s_arg[i] = bi;
             if (node_argmax) node_argmax[(long long)b * N + i] = bi;

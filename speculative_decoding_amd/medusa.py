@@ -266,6 +266,10 @@ def medusa_profile_enable(on: bool = True) -> None:
     _check("medusa_profile_enable", lib().medusa_profile_enable(1 if on else 0))
 
 
+def medusa_profile_only(kernel=None) -> None:
+    _check("medusa_profile_only", lib().medusa_profile_only(kernel.encode() if kernel else None))
+
+
 def medusa_profile_reset() -> None:
     _check("medusa_profile_reset", lib().medusa_profile_reset())
 
