@@ -823,21 +823,62 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemmBatch bt)
     }
 }
 
-// Merge of the per-tile candidate lists (each sorted best first) into the top-s.
-// Pruning: a candidate of tile t can only be in the global top-s if t is among the s tiles
-// whose best candidates rank highest (otherwise s better candidates exist, one per better
-// tile).  So the merge reads every tile's first entry, picks those s tiles, and selects the
-// top-s among their s*s entries: about n_tiles + s*s loads instead of n_tiles*s.  Both
-// selections run in one wave with wave-wide (value desc, id asc) reductions.
-constexpr int kMergeMaxTiles = 2048;
-constexpr int kMergeMaxCand = MEDUSA_MAX_TOPK * MEDUSA_MAX_TOPK;
+// Merge of the per-tile candidate lists (each sorted best first) into the top-s, in the
+// (value desc, id asc) order of `better`.
+//  1. Each thread holds the first entries (tile maxima) of tiles tid + 256 j.
+//  2. Lower bound tau on the s-th best tile maximum: in each wave the s-th best of the 64
+//     lane maxima is reached by s distinct tiles, so it is <= the s-th best overall; tau is
+//     the best of the four wave bounds.
+//  3. Tiles whose maximum is >= tau are compacted.  A wave contributes only from its s lanes
+//     at or above its own bound, so there are at most 4 * s * kMergeSlots of them.
+//  4. Their ranks by counting; rank r < s names the r-th best tile.
+//  5. Entry j of the r-th best tile has at least r + j better entries (the first entries of
+//     the r better tiles and j entries of its own list), so only r + j < s can reach the
+//     top-s, and no entry of any other tile can: s (s + 1) / 2 candidates.
+//  6. Their ranks by counting; rank < s is the output slot.
+// Each selection is one pass of independent comparisons instead of s dependent rounds, and
+// a comparison is one unsigned 64-bit compare of packed keys (merge_key).
+constexpr int kMergeSlots = 8;
+constexpr int kMergeMaxTiles = kThreads * kMergeSlots;
+constexpr int kMergeStep3 = kWaves * MEDUSA_MAX_TOPK * kMergeSlots;
+constexpr int kMergeStep5 = MEDUSA_MAX_TOPK * (MEDUSA_MAX_TOPK + 1) / 2;
+constexpr int kMergeMaxCand = kMergeStep3 > kMergeStep5 ? kMergeStep3 : kMergeStep5;
+
+// (value, id) as one key whose unsigned order is the `better` order: the high word is the
+// value's bits mapped so that unsigned order is float order (-0 folded onto +0), the low
+// word the complement of the id (lower id = larger word).  Real pairs are distinct.  Padding
+// (id INT_MAX, value -inf) gets a distinct low word per slot, below every real id's.
+constexpr uint32_t kOrdNegInf = 0x007FFFFFu;    // order word of -inf (0xFF800000)
+__device__ __forceinline__ uint64_t merge_key(float v, int id, int slot) {
+    if (id == INT_MAX) return ((uint64_t)kOrdNegInf << 32) | (uint32_t)(0x7FFFFFFF - slot);
+    const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ bool merge_key_is_pad(uint64_t k) { return (uint32_t)k < 0x80000000u; }
+__device__ __forceinline__ int merge_key_id(uint64_t k) {
+    return merge_key_is_pad(k) ? -1 : (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+__device__ __forceinline__ float merge_key_value(uint64_t k) {
+    const uint32_t o = (uint32_t)(k >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Number of keys[0, n) greater than k.
+__device__ __forceinline__ int key_rank(const uint64_t* keys, int n, uint64_t k) {
+    int r = 0;
+#pragma unroll 8
+    for (int c = 0; c < n; ++c) r += keys[c] > k ? 1 : 0;
+    return r;
+}
 
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch bt) {
-    __shared__ float tv[kMergeMaxTiles];
-    __shared__ int ti[kMergeMaxTiles];
+    __shared__ uint64_t cand[kMergeMaxCand];
+    __shared__ int cand_tile[kMergeStep3];
+    __shared__ uint64_t lane_best[kThreads];
+    __shared__ uint64_t wave_bound[kWaves];
     __shared__ int best_tiles[MEDUSA_MAX_TOPK];
-    __shared__ float cv[kMergeMaxCand];
-    __shared__ int ci[kMergeMaxCand];
+    __shared__ int n_cand, n_cand2;
     const int p = blockIdx.x / bt.M;
     const int m = blockIdx.x - p * bt.M;
     const MergeProblem& P = bt.p[p];
@@ -845,91 +886,74 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const MergeBatch b
     const int nt = P.n_tiles;
     const float* pv = P.part_val + (long long)m * nt * s;
     const int32_t* pi = P.part_idx + (long long)m * nt * s;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
 
-    // 1. every tile's best entry into LDS (tile index kept implicitly by position)
-    for (int t0 = threadIdx.x; t0 < nt; t0 += 8 * kThreads) {
-        float v[8];
-        int id[8];
+    // 1. tile maxima; slots past n_tiles are padding
+    uint64_t key[kMergeSlots];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = t0 + j * kThreads;
-            v[j] = t < nt ? pv[(long long)t * s] : -INFINITY;
-            id[j] = t < nt ? pi[(long long)t * s] : INT_MAX;
-        }
+    for (int j = 0; j < kMergeSlots; ++j) {
+        const int t = tid + kThreads * j;
+        const float v = t < nt ? pv[(long long)t * s] : -INFINITY;
+        const int id = t < nt ? pi[(long long)t * s] : INT_MAX;
+        key[j] = merge_key(v, id, t);
+    }
+    if (tid == 0) { n_cand = 0; n_cand2 = 0; }
+    // 2. lane maximum, its rank within the wave, the wave bound
+    uint64_t lb = key[0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = t0 + j * kThreads;
-            if (t < nt) { tv[t] = v[j]; ti[t] = id[j]; }
+    for (int j = 1; j < kMergeSlots; ++j) lb = key[j] > lb ? key[j] : lb;
+    lane_best[tid] = lb;
+    __syncthreads();
+    if (key_rank(lane_best + wave * kWave, kWave, lb) == s - 1) wave_bound[wave] = lb;
+    __syncthreads();
+    uint64_t tau = wave_bound[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) tau = wave_bound[w] > tau ? wave_bound[w] : tau;
+    // 3. compaction of the tiles at or above tau
+#pragma unroll
+    for (int j = 0; j < kMergeSlots; ++j) {
+        if (key[j] >= tau) {
+            const int c = atomicAdd(&n_cand, 1);
+            cand[c] = key[j];
+            cand_tile[c] = tid + kThreads * j;
         }
     }
     __syncthreads();
-    // 2. wave 0: the s tiles with the best first entries (each lane keeps its share of the
-    //    tile maxima in registers; tile t sits in lane t % 64, slot t / 64)
-    if (wave == 0) {
-        constexpr int kSlots = kMergeMaxTiles / kWave;
-        float rv_[kSlots];
-        int ri_[kSlots];
-#pragma unroll
-        for (int j = 0; j < kSlots; ++j) {
-            const int t = lane + kWave * j;
-            rv_[j] = t < nt ? tv[t] : -INFINITY;
-            ri_[j] = t < nt ? ti[t] : INT_MAX;
-        }
-        for (int round = 0; round < s; ++round) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-#pragma unroll
-            for (int j = 0; j < kSlots; ++j)
-                if (better(rv_[j], ri_[j], bv, bi)) { bv = rv_[j]; bi = ri_[j]; }
-            wave_best(bv, bi);
-            int owner_t = -1;
-#pragma unroll
-            for (int j = 0; j < kSlots; ++j)
-                if (ri_[j] == bi && bi != INT_MAX) {
-                    owner_t = lane + kWave * j;
-                    rv_[j] = -INFINITY;
-                    ri_[j] = INT_MAX;
-                }
-            if (owner_t >= 0) best_tiles[round] = owner_t;
-            if (bi == INT_MAX && lane == 0) best_tiles[round] = -1;
-        }
+    // 4. the s best tiles (padding slots name no tile)
+    const int nc = n_cand;
+    for (int c = tid; c < nc; c += kThreads) {
+        const int r = key_rank(cand, nc, cand[c]);
+        if (r < s) best_tiles[r] = cand_tile[c] < nt ? cand_tile[c] : -1;
     }
     __syncthreads();
-    // 3. their lists into LDS
-    const int nc = s * s;
-    for (int c = threadIdx.x; c < nc; c += kThreads) {
+    // 5. entries (r, j) with r + j < s of those tiles
+    for (int c = tid; c < s * s; c += kThreads) {
         const int r = c / s;
         const int j = c - r * s;
         const int t = best_tiles[r];
-        cv[c] = t >= 0 ? pv[(long long)t * s + j] : -INFINITY;
-        ci[c] = t >= 0 ? pi[(long long)t * s + j] : INT_MAX;
-    }
-    __syncthreads();
-    // 4. wave 0: the top-s of those candidates, in order
-    if (wave == 0) {
-        for (int round = 0; round < s; ++round) {
-            float bv = -INFINITY;
-            int bi = INT_MAX, bc = -1;
-            for (int c = lane; c < nc; c += kWave)
-                if (better(cv[c], ci[c], bv, bi)) { bv = cv[c]; bi = ci[c]; bc = c; }
-            float rv = bv;
-            int ri = bi;
-            wave_best(rv, ri);
-            if (lane == 0) {
-                P.out_ids[(long long)m * P.out_ld + round] = ri == INT_MAX ? -1 : ri;
-                if (P.out_vals) P.out_vals[(long long)m * P.out_ld + round] = rv;
-            }
-            if (ri == bi && bc >= 0 && ri != INT_MAX) {
-                cv[bc] = -INFINITY;
-                ci[bc] = INT_MAX;
-            }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (j < s - r && t >= 0) {
+            const uint64_t k = merge_key(pv[(long long)t * s + j], pi[(long long)t * s + j], c);
+            cand[atomicAdd(&n_cand2, 1)] = k;
         }
     }
-    for (int r = s + threadIdx.x; r < P.s_pad; r += kThreads) {
+    __syncthreads();
+    // 6. the top-s of those, in order
+    const int nc2 = n_cand2;
+    for (int c = tid; c < nc2; c += kThreads) {
+        const uint64_t k = cand[c];
+        const int r = key_rank(cand, nc2, k);
+        if (r < s) {
+            P.out_ids[(long long)m * P.out_ld + r] = merge_key_id(k);
+            if (P.out_vals) P.out_vals[(long long)m * P.out_ld + r] = merge_key_is_pad(k) ? -INFINITY : merge_key_value(k);
+        }
+    }
+    // fewer than s candidates (vocabularies smaller than s): the rest are padding
+    for (int r = nc2 + tid; r < s; r += kThreads) {
+        P.out_ids[(long long)m * P.out_ld + r] = -1;
+        if (P.out_vals) P.out_vals[(long long)m * P.out_ld + r] = -INFINITY;
+    }
+    for (int r = s + tid; r < P.s_pad; r += kThreads) {
         P.out_ids[(long long)m * P.out_ld + r] = -1;
         if (P.out_vals) P.out_vals[(long long)m * P.out_ld + r] = 0.f;
     }
