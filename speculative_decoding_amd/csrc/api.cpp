@@ -356,12 +356,11 @@ namespace {
 
 // Contraction slices for the verifier's two projections (0: direct store kernel).
 int qkv_ksplit(medusa_dtype dt, int M, int H, int Hq, int Hkv, int d) {
-    const int tiles = n_tiles_for(dt, M, EPI_PARTIAL, Hq * d, H) +
-                      2 * n_tiles_for(dt, M, EPI_PARTIAL, Hkv * d, H);
-    return store_ksplit(dt, M, H, tiles);
+    const int Ns[3] = {Hq * d, Hkv * d, Hkv * d};
+    return partial_plan(dt, M, H, Ns, 3).ksplit;
 }
 int out_ksplit(medusa_dtype dt, int M, int H, int Hq, int d) {
-    return store_ksplit(dt, M, Hq * d, n_tiles_for(dt, M, EPI_PARTIAL, H, Hq * d));
+    return partial_plan(dt, M, Hq * d, &H, 1).ksplit;
 }
 
 }  // namespace

@@ -16,6 +16,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 namespace medusa {
 
 namespace {
@@ -203,12 +205,12 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_store_kernel(const GemmB
 // Shared epilogue of the MFMA kernels: optional fp32 logits, then the per-tile argmax or
 // top-s of every input row.  acc[rt][mt][r] = Y[m0 + mt*16 + 4*lg + r][n_wave + rt*16 + ln];
 // `smem` must hold Mb * NWG floats (top-s only) and may alias the kernel's X staging area.
-template <int MT, int RT, int NWG, int EPI>
+template <int MT, int RT, int NWG, int EPI, int NWV = kWaves>
 __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBatch& bt,
                                               const floatx4 (&acc)[RT][MT], int m0, int Mb,
                                               int tile, int n_wave, int wave, int lane,
-                                              unsigned char* smem, float (&red_v)[kWaves][MT * 16],
-                                              int (&red_i)[kWaves][MT * 16]) {
+                                              unsigned char* smem, float (&red_v)[NWV][MT * 16],
+                                              int (&red_i)[NWV][MT * 16]) {
     const int ln = lane & 15;
     const int lg = lane >> 4;
     const int N = P.N;
@@ -248,11 +250,11 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBa
                 }
             }
         __syncthreads();
-        for (int m = threadIdx.x; m < Mb; m += kThreads) {
+        for (int m = threadIdx.x; m < Mb; m += NWV * kWave) {
             float bv = red_v[0][m];
             int bi = red_i[0][m];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w)
+            for (int w = 1; w < NWV; ++w)
                 if (better(red_v[w][m], red_i[w][m], bv, bi)) { bv = red_v[w][m]; bi = red_i[w][m]; }
             const long long o = (long long)(m0 + m) * P.n_tiles + tile;
             P.part_val[o] = bv;
@@ -278,7 +280,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBa
         __syncthreads();
         constexpr int PER = NWG / kWave;
         const int s = P.s;
-        for (int m = wave; m < Mb; m += kWaves) {
+        for (int m = wave; m < Mb; m += NWV) {
             float v[PER];
             int id[PER];
 #pragma unroll
@@ -462,41 +464,55 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
 #ifndef MEDUSA_RS_RTW
 #define MEDUSA_RS_RTW 4
 #endif
+#ifndef MEDUSA_RS_PF
+#define MEDUSA_RS_PF 1
+#endif
 constexpr int kRsChunk = MEDUSA_RS_CHUNK;   // contraction chunk per pass
 constexpr int kRsRtw = MEDUSA_RS_RTW;       // 16-row weight tiles per wave (argmax, top-s)
-constexpr int kRsRtwPartial = 1;            // ... for contraction slices (small weights)
+constexpr int kRsPf = MEDUSA_RS_PF;         // chunks in flight ahead of the one multiplied
+constexpr int kPartialChunk = 64;           // contraction chunk of the slice kernels
+constexpr int kWavePartialRows = 64;        // weight rows per single-wave slice tile
+#ifndef MEDUSA_RS_WAVES_ARGMAX
+#define MEDUSA_RS_WAVES_ARGMAX 8
+#endif
+#ifndef MEDUSA_RS_RTW_ARGMAX
+#define MEDUSA_RS_RTW_ARGMAX 2
+#endif
+// Argmax path (lm_head over the tree nodes): 8 waves of 32 rows per workgroup, two
+// workgroups per CU.  Measured at the 8B shape (64 nodes): 4 x 64 rows 161 us, 8 x 32 158,
+// 8 x 64 181 (one workgroup per CU; its eight-wave barrier gates every chunk), 16 x 32 176.
+constexpr int kRsWavesArgmax = MEDUSA_RS_WAVES_ARGMAX;
+constexpr int kRsRtwArgmax = MEDUSA_RS_RTW_ARGMAX;
 
-template <int MT, int EPI, int RTW>
-__global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatch bt) {
+template <int MT, int EPI, int RTW, int PF, int CH, int NWV>
+__global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmBatch bt) {
     constexpr int RT = RTW;
     constexpr int ROWS = 16 * RT;             // weight rows per wave
-    constexpr int NWG = kWaves * ROWS;
-    constexpr int XP = kRsChunk + 8;          // LDS pitch of X rows and W tiles (elements)
-    constexpr int LPR = kRsChunk / 8;         // lanes per row in one load instruction
+    constexpr int NWG = NWV * ROWS;
+    constexpr int NTH = NWV * kWave;
+    constexpr int XP = CH + 8;                // LDS pitch of X rows and W tiles (elements)
+    constexpr int LPR = CH / 8;               // lanes per row in one load instruction
     constexpr int RPI = kWave / LPR;          // rows per load instruction
     constexpr int NI = ROWS / RPI;            // 16-byte loads per lane per chunk
-    __shared__ __align__(16) bf16_t xs[MT * 16 * XP];
-    __shared__ __align__(16) bf16_t wt[kWaves][ROWS * XP];
-    __shared__ float red_v[kWaves][MT * 16];
-    __shared__ int red_i[kWaves][MT * 16];
+    constexpr int VPR = CH / 8;               // 16-byte vectors per X row chunk
+    constexpr int XV = (MT * 16 * VPR + NTH - 1) / NTH;   // ... per thread
+    // X rows past the tile land in a spare slot at the end (every thread stores)
+    __shared__ __align__(16) bf16_t xs[MT * 16 * XP + 8];
+    __shared__ __align__(16) bf16_t wt[NWV][ROWS * XP];
+    __shared__ float red_v[NWV][MT * 16];
+    __shared__ int red_i[NWV][MT * 16];
 
     const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
-    const int nks = EPI == EPI_PARTIAL ? bt.ksplit : 1;
-    const int nblocks = bt.total_tiles * n_mb * nks;
-    int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int nblocks = bt.total_tiles * n_mb;
+    const int bid = xcd_logical_block(blockIdx.x, nblocks);
     const int mb = bid % n_mb;
-    bid /= n_mb;
-    const int ksl = bid % nks;
-    const int t = bid / nks;
+    const int t = bid / n_mb;
     const GemmProblem& P = bt.p[problem_of(bt, t)];
     const int tile = t - P.tile_begin;
     const int K = bt.K;
     const int N = P.N;
-    // contraction slice of this block (whole chunks)
-    const int chunks = K / kRsChunk;
-    const int per = (chunks + nks - 1) / nks;
-    const int k_lo = min(K, ksl * per * kRsChunk);
-    const int k_hi = min(K, (ksl + 1) * per * kRsChunk);
+    const int k_lo = 0;
+    const int k_hi = K;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int ln = lane & 15;
@@ -515,11 +531,6 @@ __global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatc
         const int n = min(n_wave + RPI * i + half, N - 1);
         wsrc[i] = reinterpret_cast<const u32x4*>(W + (long long)n * K + col);
     }
-    u32x4 wr[NI];
-    auto load_w = [&](int kc) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) wr[i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
-    };
     const bf16_t* X = static_cast<const bf16_t*>(P.X);
     bf16_t* wtile = wt[wave];
 
@@ -529,91 +540,422 @@ __global__ __launch_bounds__(kThreads) void gemm_rowstream_kernel(const GemmBatc
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // X rows of the chunk are fetched one chunk ahead as well (XV vectors per thread)
-    constexpr int VPR = kRsChunk / 8;                       // 16-byte vectors per X row chunk
-    constexpr int XV = (MT * 16 * VPR + kThreads - 1) / kThreads;
+    // X vectors of this thread: rows without a source (past M, or an out-of-range gather
+    // index) read row 0 and are replaced by zeros before the LDS store
     const bf16_t* xrow_ptr[XV];
+    bool xok[XV];
     int xdst[XV];
 #pragma unroll
     for (int j = 0; j < XV; ++j) {
-        const int idx = threadIdx.x + j * kThreads;
+        const int idx = threadIdx.x + j * NTH;
         const int m = idx / VPR;
         const int c = idx - m * VPR;
-        xdst[j] = -1;
-        xrow_ptr[j] = nullptr;
-        if (m < Mb) {
-            long long r = m0 + m;
-            bool ok = true;
+        xdst[j] = m < MT * 16 ? m * XP + c * 8 : MT * 16 * XP;
+        long long r = 0;
+        bool ok = m < Mb;
+        if (ok) {
+            r = m0 + m;
             if (P.x_rows) {
                 r = P.x_rows[m0 + m];
                 ok = r >= 0 && r < bt.x_rows_bound;
+                if (!ok) r = 0;
             }
-            xdst[j] = m * XP + c * 8;
-            if (ok) xrow_ptr[j] = X + r * P.x_stride + c * 8;
         }
+        xok[j] = ok;
+        xrow_ptr[j] = X + r * P.x_stride + c * 8;
     }
-    u32x4 xr[XV];
-    auto load_x = [&](int kc) {
-#pragma unroll
-        for (int j = 0; j < XV; ++j)
-            xr[j] = xrow_ptr[j] ? *reinterpret_cast<const u32x4*>(xrow_ptr[j] + kc)
-                                : u32x4{0u, 0u, 0u, 0u};
-    };
 
-    if (k_lo < k_hi) {
-        load_w(k_lo);
-        load_x(k_lo);
+    // Ring of PF chunks in registers; chunk c of the slice lives in slot c % PF.  Every
+    // load is issued on every path (refills past the slice re-read its last chunk) so the
+    // compiler's wait counts stay exact: storing slot p waits only for slot p's loads.
+    const int n_ch = (k_hi - k_lo) / CH;
+    u32x4 wr[PF][NI];
+    u32x4 xr[PF][XV];
+    auto load = [&](int p, int c) {
+        const int kc = k_lo + min(c, n_ch - 1) * CH;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) wr[p][i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
+#pragma unroll
+        for (int j = 0; j < XV; ++j) xr[p][j] = *reinterpret_cast<const u32x4*>(xrow_ptr[j] + kc);
+    };
+    if (n_ch > 0) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) load(p, p);
     }
-    for (int kc = k_lo; kc < k_hi; kc += kRsChunk) {
+    for (int c0 = 0; c0 < n_ch; c0 += PF)
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int c = c0 + p;
+        if (c >= n_ch) break;
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < XV; ++j)
-            if (xdst[j] >= 0) *reinterpret_cast<u32x4*>(xs + xdst[j]) = xr[j];
+        for (int j = 0; j < XV; ++j) {
+            const u32x4 v = xok[j] ? xr[p][j] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(xs + xdst[j]) = v;
+        }
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            *reinterpret_cast<u32x4*>(wtile + (RPI * i + half) * XP + col) = wr[i];
+            *reinterpret_cast<u32x4*>(wtile + (RPI * i + half) * XP + col) = wr[p][i];
         __syncthreads();
-        if (kc + kRsChunk < k_hi) {
-            load_w(kc + kRsChunk);
-            load_x(kc + kRsChunk);
-        }
+        load(p, c + PF);
 #pragma unroll
-        for (int ks = 0; ks < kRsChunk; ks += 32) {
+        for (int ks = 0; ks < CH; ks += 32) {
             Frag<bf16_t> wf[RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) wf[rt].load(wtile + (rt * 16 + ln) * XP + ks + 8 * lg);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                Frag<bf16_t> xf;
-                const int m = mt * 16 + ln;
-                if (m < Mb) xf.load(xs + m * XP + ks + 8 * lg);
-                else xf.zero();
+                Frag<bf16_t> xf;       // rows past Mb hold zeros
+                xf.load(xs + (mt * 16 + ln) * XP + ks + 8 * lg);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) mma(acc[rt][mt], xf, wf[rt]);
             }
         }
     }
-    if (EPI == EPI_PARTIAL) {
-        float* part = P.part_val + (long long)ksl * bt.M * N;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int n = n_wave + rt * 16 + ln;
-            if (n >= N) continue;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + mt * 16 + 4 * lg + r;
-                    if (m < bt.M) part[(long long)m * N + n] = acc[rt][mt][r];
-                }
-        }
-        return;
-    }
     // the top-s epilogue needs Mb * NWG floats of scratch: the W tiles are free by now
     static_assert(EPI != EPI_TOPS || sizeof(wt) >= 16 * NWG * sizeof(float), "top-s scratch");
     __syncthreads();
-    tile_epilogue<MT, RT, NWG, EPI>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane,
-                                    reinterpret_cast<unsigned char*>(&wt[0][0]), red_v, red_i);
+    tile_epilogue<MT, RT, NWG, EPI, NWV>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane,
+                                         reinterpret_cast<unsigned char*>(&wt[0][0]), red_v, red_i);
+}
+
+// Single-wave contraction slices for the verifier's projections (many input rows, small
+// weights).  One wave per workgroup owns 16*RT weight rows, MT*16 input rows and one
+// contraction slice, so no step waits for another wave: the weight chunk is transposed
+// through a wave-private, double-buffered LDS tile (the store of chunk c+1 overlaps the
+// products of chunk c; one single-wave barrier per chunk) and the input rows are loaded
+// straight from the cache in the MFMA operand layout (16 input rows x 8 contraction
+// elements per lane and step).  Weight and input chunks run PF chunks ahead in registers.
+// The slice sums go to part_val like the row-streaming kernel's, and the same finalize
+// pass sums them.
+template <int MT, int RT, int PF, int CH>
+__global__ __launch_bounds__(kWave) void gemm_wave_partial_kernel(const GemmBatch bt) {
+    constexpr int ROWS = 16 * RT;
+    constexpr int XP = CH + 8;                // LDS pitch of a weight row (elements)
+    constexpr int LPR = CH / 8;               // lanes per weight row per load instruction
+    constexpr int RPI = kWave / LPR;          // weight rows per load instruction
+    constexpr int NI = ROWS / RPI;            // weight loads per lane per chunk
+    constexpr int KS = CH / 32;               // MFMA steps per chunk
+    constexpr int XL = MT * KS;               // input loads per lane per chunk
+    static_assert(ROWS % RPI == 0, "rows per load");
+    __shared__ __align__(16) bf16_t wt[2][ROWS * XP];
+
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    const int nks = bt.ksplit;
+    const int nblocks = bt.total_tiles * n_mb * nks;
+    int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int mb = bid % n_mb;
+    bid /= n_mb;
+    const int ksl = bid % nks;
+    const int t = bid / nks;
+    const GemmProblem& P = bt.p[problem_of(bt, t)];
+    const int tile = t - P.tile_begin;
+    const int K = bt.K;
+    const int N = P.N;
+    const int chunks = K / CH;
+    const int per = (chunks + nks - 1) / nks;
+    const int c_lo = min(chunks, ksl * per);
+    const int n_ch = min(chunks, (ksl + 1) * per) - c_lo;
+    const int k_lo = c_lo * CH;
+    const int lane = threadIdx.x;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int n0 = tile * ROWS;
+    const int m0 = mb * MT * 16;
+
+    const bf16_t* W = static_cast<const bf16_t*>(P.W);
+    const int half = lane / LPR;
+    const int col = (lane % LPR) * 8;
+    const u32x4* wsrc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int n = min(n0 + RPI * i + half, N - 1);
+        wsrc[i] = reinterpret_cast<const u32x4*>(W + (long long)n * K + k_lo + col);
+    }
+    // input row of m-tile mt for this lane: rows without a source read row 0, zeroed later
+    const bf16_t* X = static_cast<const bf16_t*>(P.X);
+    const bf16_t* xsrc[MT];
+    bool xok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = m0 + mt * 16 + ln;
+        long long r = 0;
+        bool ok = m < bt.M;
+        if (ok) {
+            r = m;
+            if (P.x_rows) {
+                r = P.x_rows[m];
+                ok = r >= 0 && r < bt.x_rows_bound;
+                if (!ok) r = 0;
+            }
+        }
+        xok[mt] = ok;
+        xsrc[mt] = X + r * P.x_stride + k_lo + 8 * lg;
+    }
+
+    floatx4 acc[RT][MT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // rings: chunk j in slot j % PF; every load is issued on every path (chunks past the
+    // slice re-read its last one) so the compiler's wait counts stay exact
+    u32x4 wr[PF][NI];
+    u32x4 xr[PF][XL];
+    auto load_w = [&](int p, int c) {
+        const int kc = min(c, n_ch - 1) * CH;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) wr[p][i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
+    };
+    auto load_x = [&](int p, int c) {
+        const int kc = min(c, n_ch - 1) * CH;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                xr[p][mt * KS + ks] = *reinterpret_cast<const u32x4*>(xsrc[mt] + kc + 32 * ks);
+    };
+    auto store_w = [&](int p, int buf) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            *reinterpret_cast<u32x4*>(&wt[buf][(RPI * i + half) * XP + col]) = wr[p][i];
+    };
+    if (n_ch > 0) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            load_w(p, p);
+            load_x(p, p);
+        }
+        store_w(0, 0);
+        load_w(0, PF);
+        __syncthreads();
+        for (int c0 = 0; c0 < n_ch; c0 += 2 * PF)
+#pragma unroll
+        for (int u = 0; u < 2 * PF; ++u) {
+            const int c = c0 + u;
+            if (c >= n_ch) break;
+            const int ps = u % PF;               // slot of chunk c
+            const int pn = (u + 1) % PF;         // slot of chunk c + 1
+            // weights of chunk c+1 into the other buffer, then refill their slot
+            if (c + 1 < n_ch) store_w(pn, (u + 1) & 1);
+            load_w(pn, c + 1 + PF);
+            const bf16_t* wb = wt[u & 1];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Frag<bf16_t> wf[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) wf[rt].load(wb + (rt * 16 + ln) * XP + 32 * ks + 8 * lg);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    Frag<bf16_t> xf;
+                    xf.v = xok[mt] ? xr[ps][mt * KS + ks] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) mma(acc[rt][mt], xf, wf[rt]);
+                }
+            }
+            load_x(ps, c + PF);
+            __syncthreads();
+        }
+    }
+    float* part = P.part_val + (long long)ksl * bt.M * N;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int n = n0 + rt * 16 + ln;
+        if (n >= N) continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + mt * 16 + 4 * lg + r;
+                if (m < bt.M) part[(long long)m * N + n] = acc[rt][mt][r];
+            }
+    }
+}
+
+// One workgroup per compute unit for the verifier's projections.  Every CU's vector memory
+// path moves only so many bytes per second (about 27 GB/s per CU at full HBM rate), so a
+// small, latency-exposed GEMM streams fastest when each of the 256 CUs carries the same
+// weight bytes and little else.  A workgroup owns NW*32 weight rows (a wave per 32 rows;
+// the rows may run across the batch's problems, whose sizes are multiples of 32) and one
+// contraction slice: it stages the slice of the (gathered) input rows in LDS once, then
+// every wave streams its rows like gemm_wave_partial_kernel (register ring, private
+// double-buffered transpose) with the input operands read from the shared slice.
+constexpr int kCuRt = 2;                     // 16-row tiles per wave
+constexpr int kCuChunk = 64;
+constexpr int kCuXv = 16;                    // staged input vectors per thread per batch
+
+template <int NW, int PF>
+__global__ __launch_bounds__(NW * kWave) void gemm_cu_partial_kernel(const GemmBatch bt, int rows_total) {
+    constexpr int MT = 4;
+    constexpr int RT = kCuRt;
+    constexpr int CH = kCuChunk;
+    constexpr int ROWS = 16 * RT;
+    constexpr int R = NW * ROWS;
+    constexpr int XP = CH + 8;
+    constexpr int LPR = CH / 8;
+    constexpr int RPI = kWave / LPR;
+    constexpr int NI = ROWS / RPI;
+    constexpr int KS = CH / 32;
+    constexpr int NT = NW * kWave;
+    extern __shared__ __align__(16) unsigned char dyn_smem[];
+
+    const int nks = bt.ksplit;
+    const int n_rt = (rows_total + R - 1) / R;
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    const int nblocks = n_rt * n_mb * nks;
+    int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int mb = bid % n_mb;
+    bid /= n_mb;
+    const int ksl = bid % nks;
+    const int rtile = bid / nks;
+    const int K = bt.K;
+    const int chunks = K / CH;
+    const int per = (chunks + nks - 1) / nks;
+    const int c_lo = min(chunks, ksl * per);
+    const int n_ch = min(chunks, (ksl + 1) * per) - c_lo;
+    const int k_lo = c_lo * CH;
+    const int XPK = per * CH + 8;                            // LDS pitch of the input slice
+    bf16_t* xs = reinterpret_cast<bf16_t*>(dyn_smem);        // [MT*16][XPK]
+    bf16_t* wt_all = xs + MT * 16 * XPK;                     // [NW][2][ROWS*XP]
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int m0 = mb * MT * 16;
+
+    // this wave's rows in the concatenation of the problems
+    const int g0 = rtile * R + wave * ROWS;
+    int p = 0, rb = 0;
+    while (p < bt.n_problems - 1 && g0 >= rb + bt.p[p].N) rb += bt.p[p++].N;
+    const GemmProblem& P = bt.p[p];
+    const bool active = g0 < rows_total;
+    const int n0 = active ? g0 - rb : 0;
+    const int my_ch = active ? n_ch : 0;        // waves past the last row stream nothing
+    const int N = P.N;
+
+    const bf16_t* W = static_cast<const bf16_t*>(P.W);
+    const int half = lane / LPR;
+    const int col = (lane % LPR) * 8;
+    const u32x4* wsrc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int n = min(n0 + RPI * i + half, N - 1);
+        wsrc[i] = reinterpret_cast<const u32x4*>(W + (long long)n * K + k_lo + col);
+    }
+    u32x4 wr[PF][NI];
+    auto load_w = [&](int q, int c) {
+        const int kc = min(c, my_ch - 1) * CH;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) wr[q][i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
+    };
+    bf16_t* wt = wt_all + wave * 2 * ROWS * XP;
+    auto store_w = [&](int q, int buf) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            *reinterpret_cast<u32x4*>(&wt[buf * ROWS * XP + (RPI * i + half) * XP + col]) = wr[q][i];
+    };
+    if (my_ch > 0) {
+#pragma unroll
+        for (int q = 0; q < PF; ++q) load_w(q, q);
+    }
+
+    // input slice: rows m0.. of the (shared) input, columns k_lo .. k_lo + n_ch*CH; rows
+    // without a source are zero.  The gather indices are resolved once into LDS, then every
+    // row load is issued unconditionally (kCuXv per thread before their stores), so the
+    // loads overlap instead of waiting one by one.
+    {
+        __shared__ int xrow[MT * 16];
+        const GemmProblem& P0 = bt.p[0];
+        if (threadIdx.x < MT * 16) {
+            const int m = m0 + threadIdx.x;
+            int r = -1;
+            if (m < bt.M) {
+                r = m;
+                if (P0.x_rows) {                 // gathered rows: out-of-range indices read zeros
+                    r = P0.x_rows[m];
+                    if (r < 0 || r >= bt.x_rows_bound) r = -1;
+                }
+            }
+            xrow[threadIdx.x] = r;
+        }
+        __syncthreads();
+        const bf16_t* X = static_cast<const bf16_t*>(P0.X) + k_lo;
+        const int vpr = n_ch * CH / 8;
+        const int total = MT * 16 * vpr;
+        for (int base = 0; base < total; base += NT * kCuXv) {
+            u32x4 v[kCuXv];
+            int dst[kCuXv];
+#pragma unroll
+            for (int j = 0; j < kCuXv; ++j) {
+                const int idx = min(base + j * NT + (int)threadIdx.x, total - 1);
+                const int m = idx / vpr;
+                const int c = idx - m * vpr;
+                const int r = xrow[m];
+                dst[j] = base + j * NT + (int)threadIdx.x < total ? (r >= 0 ? m * XPK + c * 8 : -(m * XPK + c * 8) - 1) : INT_MIN;
+                v[j] = *reinterpret_cast<const u32x4*>(X + (long long)max(r, 0) * P0.x_stride + c * 8);
+            }
+#pragma unroll
+            for (int j = 0; j < kCuXv; ++j) {
+                if (dst[j] == INT_MIN) continue;
+                const bool ok = dst[j] >= 0;
+                *reinterpret_cast<u32x4*>(xs + (ok ? dst[j] : -dst[j] - 1)) = ok ? v[j] : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    floatx4 acc[RT][MT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    if (my_ch > 0) {
+        store_w(0, 0);
+        load_w(0, PF);
+    }
+    __syncthreads();
+    if (my_ch > 0) {
+        for (int c0 = 0; c0 < my_ch; c0 += 2 * PF)
+#pragma unroll
+        for (int u = 0; u < 2 * PF; ++u) {
+            const int c = c0 + u;
+            if (c >= my_ch) break;
+            const int pn = (u + 1) % PF;
+            if (c + 1 < my_ch) store_w(pn, (u + 1) & 1);
+            load_w(pn, c + 1 + PF);
+            const bf16_t* wb = wt + (u & 1) * ROWS * XP;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Frag<bf16_t> wf[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) wf[rt].load(wb + (rt * 16 + ln) * XP + 32 * ks + 8 * lg);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    Frag<bf16_t> xf;
+                    xf.load(xs + (mt * 16 + ln) * XPK + c * CH + 32 * ks + 8 * lg);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) mma(acc[rt][mt], xf, wf[rt]);
+                }
+            }
+            // wave-private buffer: a single-wave ordering point suffices
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+    if (!active) return;
+    float* part = P.part_val + (long long)ksl * bt.M * N;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int n = n0 + rt * 16 + ln;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + mt * 16 + 4 * lg + r;
+                if (m < bt.M) part[(long long)m * N + n] = acc[rt][mt][r];
+            }
+    }
 }
 
 // Sum the contraction slices of every (m, n) in slice order and apply the store epilogue:
@@ -635,11 +977,30 @@ __global__ __launch_bounds__(kThreads) void splitk_finalize_kernel(const GemmBat
     const int m = (int)(q / qpr);
     const int n0 = (int)(q - (long long)m * qpr) * 4;
     float y[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < bt.ksplit; ++ks) {
-        const float* part = P.part_val + ((long long)ks * bt.M + m) * N;
+    if (N % 4 == 0) {
+        // one 16-byte load per slice, all slices in flight before the (ordered) sum
+        constexpr int kMaxSlices = 16;
+        floatx4 sv[kMaxSlices];
+        const floatx4* base = reinterpret_cast<const floatx4*>(P.part_val + (long long)m * N + n0);
+        const long long stride = (long long)bt.M * N / 4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (n0 + j < N) y[j] += part[n0 + j];
+        for (int ks = 0; ks < kMaxSlices; ++ks)
+            if (ks < bt.ksplit) sv[ks] = base[ks * stride];
+#pragma unroll
+        for (int ks = 0; ks < kMaxSlices; ++ks)
+            if (ks < bt.ksplit)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] += sv[ks][j];
+        for (int ks = kMaxSlices; ks < bt.ksplit; ++ks)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] += base[ks * stride][j];
+    } else {
+        for (int ks = 0; ks < bt.ksplit; ++ks) {
+            const float* part = P.part_val + ((long long)ks * bt.M + m) * N;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n0 + j < N) y[j] += part[n0 + j];
+        }
     }
     const T* bias = static_cast<const T*>(P.bias);
     const T* res = static_cast<const T*>(P.res);
@@ -1019,8 +1380,9 @@ bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
 
 int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
-    if (epi == EPI_PARTIAL) return kWaves * 16 * kRsRtwPartial;
-    if (rowstream_eligible(dt, epi, M, K)) return kWaves * 16 * kRsRtw;
+    if (epi == EPI_PARTIAL) return kWavePartialRows;
+    if (rowstream_eligible(dt, epi, M, K))
+        return epi == EPI_ARGMAX ? kRsWavesArgmax * 16 * kRsRtwArgmax : kWaves * 16 * kRsRtw;
     int rt;
     if (dt == MEDUSA_BF16)
         rt = epi == EPI_TOPS ? StreamCfg<bf16_t, EPI_TOPS>::RT : StreamCfg<bf16_t, EPI_ARGMAX>::RT;
@@ -1066,25 +1428,25 @@ bool gemv_eligible(medusa_dtype dt, int epi, const GemmBatch& bt) {
 
 }  // namespace
 
-template <int MT, int EPI, int RTW>
+template <int MT, int EPI, int RTW, int PF, int CH, int NWV>
 hipError_t launch_rowstream_t(GemmBatch& bt, hipStream_t stream) {
     const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
-    const int nks = EPI == EPI_PARTIAL ? bt.ksplit : 1;
-    hipLaunchKernelGGL((gemm_rowstream_kernel<MT, EPI, RTW>), dim3(bt.total_tiles * n_mb * nks),
-                       dim3(kThreads), 0, stream, bt);
+    hipLaunchKernelGGL((gemm_rowstream_kernel<MT, EPI, RTW, PF, CH, NWV>),
+                       dim3(bt.total_tiles * n_mb), dim3(NWV * kWave), 0, stream, bt);
     return hipGetLastError();
 }
 
+template <int EPI, int RTW, int PF, int CH, int NWV>
+hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
+    if (bt.M <= 16) return launch_rowstream_t<1, EPI, RTW, PF, CH, NWV>(bt, stream);
+    if (bt.M <= 32) return launch_rowstream_t<2, EPI, RTW, PF, CH, NWV>(bt, stream);
+    return launch_rowstream_t<4, EPI, RTW, PF, CH, NWV>(bt, stream);
+}
+
 hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
-    if (epi == EPI_TOPS) return launch_rowstream_t<1, EPI_TOPS, kRsRtw>(bt, stream);
-    if (epi == EPI_PARTIAL) {
-        if (bt.M <= 16) return launch_rowstream_t<1, EPI_PARTIAL, kRsRtwPartial>(bt, stream);
-        if (bt.M <= 32) return launch_rowstream_t<2, EPI_PARTIAL, kRsRtwPartial>(bt, stream);
-        return launch_rowstream_t<4, EPI_PARTIAL, kRsRtwPartial>(bt, stream);
-    }
-    if (bt.M <= 16) return launch_rowstream_t<1, EPI_ARGMAX, kRsRtw>(bt, stream);
-    if (bt.M <= 32) return launch_rowstream_t<2, EPI_ARGMAX, kRsRtw>(bt, stream);
-    return launch_rowstream_t<4, EPI_ARGMAX, kRsRtw>(bt, stream);
+    if (epi == EPI_TOPS)
+        return launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunk, kWaves>(bt, stream);
+    return launch_rowstream_m<EPI_ARGMAX, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
 }
 
 // Row-streaming MFMA path: bf16, contraction a multiple of its 256-wide chunk, argmax or
@@ -1094,15 +1456,108 @@ bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K) {
     return epi == EPI_ARGMAX || (epi == EPI_TOPS && M > 2);
 }
 
-int store_ksplit(medusa_dtype dt, int M, int K, int tiles) {
-    if (dt != MEDUSA_BF16 || M <= 16 || K % kRsChunk != 0) return 0;
+#ifndef MEDUSA_KSPLIT_WG
+#define MEDUSA_KSPLIT_WG 384
+#endif
+#ifndef MEDUSA_CU_PF
+#define MEDUSA_CU_PF 4
+#endif
+#ifndef MEDUSA_WAVE_PF
+#define MEDUSA_WAVE_PF 2
+#endif
+constexpr int kPlanCus = 256;           // compute units the plan balances over (MI355X)
+constexpr size_t kCuLdsBudget = 150 * 1024;
+
+size_t cu_partial_lds(int nw, int K, int ks) {
+    const int slice = K / ks;
+    return (size_t)64 * (slice + 8) * 2 + (size_t)nw * 2 * 16 * kCuRt * (kCuChunk + 8) * 2;
+}
+
+PartialPlan partial_plan(medusa_dtype dt, int M, int K, const int* Ns, int n) {
+    PartialPlan pl{0, 0};
+    if (dt != MEDUSA_BF16 || M <= 16 || K % kPartialChunk != 0) return pl;
+    long long rows = 0;
+    bool rows32 = true;
+    for (int i = 0; i < n; ++i) {
+        rows += Ns[i];
+        rows32 = rows32 && Ns[i] % (16 * kCuRt) == 0;
+    }
     const int n_mb = (M + 63) / 64;
-    const int want = (384 + tiles * n_mb - 1) / (tiles * n_mb);   // about 384 workgroups
-    return max(1, min(want, min(8, K / kRsChunk)));
+    if (rows32 && K % kCuChunk == 0) {
+        // one workgroup per CU: minimise the bytes the busiest CU moves (weights, staged
+        // input slice, slice sums) plus its share of the finalize pass
+        double best = 0;
+        static const int kWavesOpt[] = {2, 4, 6, 8};
+        static const int kSplitOpt[] = {1, 2, 4, 8, 16};
+        for (int nw : kWavesOpt)
+            for (int ks : kSplitOpt) {
+                if (K % (kCuChunk * ks) != 0 || cu_partial_lds(nw, K, ks) > kCuLdsBudget) continue;
+                const long long R = 16LL * kCuRt * nw;
+                const long long wgs = (rows + R - 1) / R * ks * n_mb;
+                const long long rounds = (wgs + kPlanCus - 1) / kPlanCus;
+                const double slice = (double)K / ks;
+                const double per_wg = R * slice * 2 + 64 * slice * 2 + (ks > 1 ? R * 64 * 4 : 0);
+                const double fin = ks > 1 ? (double)ks * M * rows * 4 / kPlanCus : 0;
+                const double cost = rounds * per_wg + fin;
+                if (pl.waves == 0 || cost < best) {
+                    best = cost;
+                    pl.waves = nw;
+                    pl.ksplit = ks;
+                }
+            }
+        if (pl.waves) return pl;
+    }
+    // per-problem 64-row tiles on the single-wave kernel
+    long long tiles = 0;
+    for (int i = 0; i < n; ++i) tiles += (Ns[i] + 63) / 64;
+    const long long want = (MEDUSA_KSPLIT_WG + tiles * n_mb - 1) / (tiles * n_mb);
+    pl.ksplit = (int)std::max(1LL, std::min(want, (long long)std::min(16, K / kPartialChunk)));
+    return pl;
+}
+
+template <int MT>
+hipError_t launch_wave_partial(GemmBatch& bt, hipStream_t stream) {
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    static_assert(kWavePartialRows == 16 * 4, "tile rows of the single-wave kernel");
+    hipLaunchKernelGGL((gemm_wave_partial_kernel<MT, 4, MEDUSA_WAVE_PF, kPartialChunk>),
+                       dim3(bt.total_tiles * n_mb * bt.ksplit), dim3(kWave), 0, stream, bt);
+    return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_cu_partial(GemmBatch& bt, int rows, hipStream_t stream) {
+    auto kern = gemm_cu_partial_kernel<NW, MEDUSA_CU_PF>;
+    const size_t lds = cu_partial_lds(NW, bt.K, bt.ksplit);
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kCuLdsBudget);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int R = 16 * kCuRt * NW;
+    const int n_mb = (bt.M + 63) / 64;
+    hipLaunchKernelGGL(kern, dim3((rows + R - 1) / R * n_mb * bt.ksplit), dim3(NW * kWave), lds,
+                       stream, bt, rows);
+    return hipGetLastError();
 }
 
 hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& bt, hipStream_t stream) {
-    hipError_t e = launch_rowstream(EPI_PARTIAL, bt, stream);
+    int Ns[kMaxProblems];
+    int rows = 0;
+    for (int p = 0; p < bt.n_problems; ++p) rows += (Ns[p] = bt.p[p].N);
+    const PartialPlan pl = partial_plan(dt, bt.M, bt.K, Ns, bt.n_problems);
+    if (pl.ksplit != bt.ksplit) return hipErrorInvalidValue;      // the caller sized part_val
+    hipError_t e;
+    switch (pl.waves) {
+    case 2: e = launch_cu_partial<2>(bt, rows, stream); break;
+    case 4: e = launch_cu_partial<4>(bt, rows, stream); break;
+    case 6: e = launch_cu_partial<6>(bt, rows, stream); break;
+    case 8: e = launch_cu_partial<8>(bt, rows, stream); break;
+    default:
+        e = bt.M <= 16 ? launch_wave_partial<1>(bt, stream)
+          : bt.M <= 32 ? launch_wave_partial<2>(bt, stream) : launch_wave_partial<4>(bt, stream);
+    }
     if (e != hipSuccess) return e;
     long long quads = 0;
     for (int p = 0; p < bt.n_problems; ++p) quads += (long long)bt.M * ((bt.p[p].N + 3) / 4);

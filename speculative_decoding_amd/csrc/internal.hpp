@@ -63,11 +63,16 @@ int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K);
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& batch, hipStream_t stream);
 
 // Store GEMMs with many input rows (the verifier's projections) run as contraction slices
-// on the row-streaming kernel (EPI_PARTIAL) plus a finalize pass that sums the slices in
-// order and applies the store epilogue.  store_ksplit() > 0 selects that path; it returns
-// the number of slices for `tiles` weight tiles (rows per tile from gemm_rows_per_tile
-// with EPI_PARTIAL).  The caller points each problem's part_val at ksplit*M*N floats.
-int store_ksplit(medusa_dtype dt, int M, int K, int tiles);
+// (EPI_PARTIAL) plus a finalize pass that sums the slices in order and applies the store
+// epilogue.  partial_plan() picks the slice count and the kernel shape from the problem
+// sizes alone (the same answer for the workspace query and the launch); ksplit == 0 means
+// no split (the direct store kernel).  The caller points each problem's part_val at
+// ksplit*M*N floats and sets batch.ksplit to the plan's.
+struct PartialPlan {
+    int ksplit;     // contraction slices; 0: not applicable
+    int waves;      // waves per workgroup of the one-workgroup-per-CU kernel; 0: single-wave kernel
+};
+PartialPlan partial_plan(medusa_dtype dt, int M, int K, const int* Ns, int n);
 hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& batch, hipStream_t stream);
 
 // ------------------------------------------------------------------ top-s merge

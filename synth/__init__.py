@@ -6,7 +6,8 @@ head, tree, attention, verification or acceptance step is computed here.  Both
 the CPU oracle and the GPU path consume the exact bytes it produces.
 """
 from .configs import CONFIGS, Config, get_config
-from .gen import Inputs, make_inputs, bf16_bits_to_f32, f32_to_bf16_bits
+from .gen import (Inputs, bf16_bits_to_f32, f32_to_bf16_bits, integers, make_inputs,
+                  normal_bf16)
 
 __all__ = ["CONFIGS", "Config", "get_config", "Inputs", "make_inputs",
-           "bf16_bits_to_f32", "f32_to_bf16_bits"]
+           "bf16_bits_to_f32", "f32_to_bf16_bits", "normal_bf16", "integers"]

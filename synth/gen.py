@@ -79,6 +79,20 @@ def _normal_matrix(seed: int, cfg: Config, tensor: str, rows: int, cols: int, si
     return out
 
 
+def normal_bf16(seed: int, tag: str, shape, sigma: float) -> np.ndarray:
+    """A standalone seeded N(0, sigma) tensor of any shape as bf16 bit patterns (uint16),
+    for unit-level parity cases that need no full configuration."""
+    g = _rng(seed, "standalone", tag)
+    buf = g.standard_normal(tuple(shape), dtype=np.float32)
+    buf *= np.float32(sigma)
+    return f32_to_bf16_bits(buf)
+
+
+def integers(seed: int, tag: str, low: int, high: int, shape) -> np.ndarray:
+    """A standalone seeded uniform integer tensor in [low, high) (int32)."""
+    return _rng(seed, "standalone", tag).integers(low, high, size=tuple(shape)).astype(np.int32)
+
+
 @dataclass
 class Inputs:
     """All tensors of one Medusa decode step, as produced by the generator.
