@@ -10,9 +10,11 @@ Inputs are resident in HBM before timing starts.  Prints one JSON line on stdout
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -21,6 +23,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 DOMINANT = "heads_vocab"        # the kernel with most of the step's bytes (A2+A3)
+# HBM bytes of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, valid while
+# the sources it was measured on are unchanged (their hash is recorded beside the figure)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "heads_vocab_8b_traffic.md")
+KERNEL_SOURCES = ("speculative_decoding_amd/csrc/gemm.hip", "speculative_decoding_amd/csrc/common.hpp",
+                  "speculative_decoding_amd/csrc/internal.hpp")
 METRIC = "Medusa verify steps/s + tokens/s and achieved HBM GB/s at 8B shape, 1 GPU"
 
 WORKLOADS = {
@@ -57,6 +64,30 @@ def algorithmic_bytes(cfg, n_nodes: int, prefix_total: int) -> dict:
     }
     parts["total"] = sum(parts.values())
     return parts
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config_name: str):
+    """Bytes per launch of the dominant kernel from the committed counter summary, or None
+    when there is none for this workload or the kernel sources changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, re.M))
+    if fields.get("workload") != config_name or fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_info():
@@ -106,6 +137,9 @@ def main() -> int:
     ap.add_argument("--config", default="8b", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run an elementwise kernel that reads and writes this many MiB once before "
+                         "the timed region (known sizes to calibrate rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -147,6 +181,14 @@ def main() -> int:
         step.run(bootstrap_root=False, keep_u=False)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)       # a fill kernel: writes n
+        dst = torch.empty_like(src)
+        torch.add(src, 1, out=dst)                                # a kernel reading n, writing n
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {n} bytes read and written")
+        del src, dst
 
     # timed region: exactly K steps; the dominant kernel's launches are bracketed by HIP
     # events on their own stream (two event records per step)
@@ -180,6 +222,9 @@ def main() -> int:
             kernels[name] = {"avg_us": 1e3 * ms / n, "launches": n}
 
     res = step.results()
+    props = torch.cuda.get_device_properties(dev)
+    device = {"name": props.name, "cus": props.multi_processor_count,
+              "arch": getattr(props, "gcnArchName", ""), "hbm_gib": round(props.total_memory / 2**30)}
     a = [int(x) for x in res["accept_len"]]
     prefix_total = int(np.minimum(inp.prefix_lens, cfg.Lcap).sum())
     ab = algorithmic_bytes(cfg, n_nodes, prefix_total)
@@ -199,7 +244,8 @@ def main() -> int:
         hv = 1e3 * dom_ms / dom_n
         achieved = ab[DOMINANT] / (hv * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": DOMINANT,
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(cfg.name),
+                "kernel": DOMINANT,
                 "bytes_per_launch": ab[DOMINANT], "avg_us": hv, "launches": dom_n}
     out = {
         "metric": METRIC,
@@ -225,6 +271,7 @@ def main() -> int:
         "algorithmic_bytes_per_step": ab["total"],
         "roofline": roof,
         "kernels": kernels,
+        "device": device,
         "kernels_note": "per-kernel averages from a second pass of the same steps with every "
                         "launch event-timed (not the timed region)",
     }
