@@ -23,6 +23,9 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: kernels that rescale their accumulators between
+    # MFMAs (attention's online softmax) otherwise copy them out of and back into AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
 ]
 

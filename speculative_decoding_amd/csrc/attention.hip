@@ -18,6 +18,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace medusa {
 
 namespace {
@@ -54,11 +56,9 @@ template <> struct Vt4<bf16_t> {
         uint32_t wh[4], wl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bf16_t h0 = f32_to_bf16(p[2 * i]), h1 = f32_to_bf16(p[2 * i + 1]);
-            const bf16_t l0 = f32_to_bf16(p[2 * i] - bf16_to_f32(h0));
-            const bf16_t l1 = f32_to_bf16(p[2 * i + 1] - bf16_to_f32(h1));
-            wh[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            wl[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            wh[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+            wl[i] = pack_bf16x2(p[2 * i] - __uint_as_float(wh[i] << 16),
+                                p[2 * i + 1] - __uint_as_float(wh[i] & 0xFFFF0000u));
         }
         hi.v = u32x4{wh[0], wh[1], wh[2], wh[3]};
         lo.v = u32x4{wl[0], wl[1], wl[2], wl[3]};
@@ -149,46 +149,47 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
     // j+1 are in flight while block j is multiplied out of LDS.
     constexpr int VPR = D / EPV;                 // 16-byte vectors per key row
     constexpr int NV = kKeys * VPR / kThreads;   // vectors per thread per block
-    u32x4 kr[NV], vr[NV];
     // K: consecutive threads read consecutive 16-byte pieces of a key row (coalesced, and
     // stored row-major).  V: consecutive threads take consecutive keys of one 16-byte column
     // piece, so the transposed scalar LDS stores of a wave hit 64 consecutive keys of one
     // V^T row (no bank conflicts) instead of 16 rows that all map to the same bank.
-    auto fetch = [&](int kb0) {
+    int kkey[NV], koff[NV], vkey[NV], voff[NV];
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int idx = threadIdx.x + j * kThreads;
-            const int key = idx / VPR;
-            const int c = idx - key * VPR;
-            const int vkey = idx % kKeys;
-            const int vc = idx / kKeys;
-            kr[j] = u32x4{0u, 0u, 0u, 0u};
-            vr[j] = kr[j];
-            if (kb0 + key < k_end)
-                kr[j] = *reinterpret_cast<const u32x4*>(ksrc + (long long)(kb0 + key) * kstride + c * EPV);
-            if (kb0 + vkey < k_end)
-                vr[j] = *reinterpret_cast<const u32x4*>(vsrc + (long long)(kb0 + vkey) * kstride + vc * EPV);
+    for (int j = 0; j < NV; ++j) {
+        const int idx = threadIdx.x + j * kThreads;
+        kkey[j] = idx / VPR;
+        koff[j] = kkey[j] * (int)kstride + (idx - kkey[j] * VPR) * EPV;
+        vkey[j] = idx % kKeys;
+        voff[j] = vkey[j] * (int)kstride + (idx / kKeys) * EPV;
+    }
+    u32x4 kr[NV], vr[NV];
+    auto fetch = [&](int kb0) {
+        const T* kb = ksrc + (long long)kb0 * kstride;
+        const T* vb = vsrc + (long long)kb0 * kstride;
+        if (kb0 + kKeys <= k_end) {          // a whole block: no per-key checks
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                kr[j] = *reinterpret_cast<const u32x4*>(kb + koff[j]);
+                vr[j] = *reinterpret_cast<const u32x4*>(vb + voff[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                kr[j] = u32x4{0u, 0u, 0u, 0u};
+                vr[j] = kr[j];
+                if (kb0 + kkey[j] < k_end) kr[j] = *reinterpret_cast<const u32x4*>(kb + koff[j]);
+                if (kb0 + vkey[j] < k_end) vr[j] = *reinterpret_cast<const u32x4*>(vb + voff[j]);
+            }
         }
     };
-    fetch(k_begin);
-    for (int kb0 = k_begin; kb0 < k_end; kb0 += kKeys) {
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int idx = threadIdx.x + j * kThreads;
-            const int key = idx / VPR;
-            const int c = idx - key * VPR;
-            *reinterpret_cast<u32x4*>(Ks + key * KP + c * EPV) = kr[j];
-            const int vkey = idx % kKeys;
-            const int vc = idx / kKeys;
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) Vt[(vc * EPV + e) * VP + vkey] = Vt4<T>::elem(vr[j], e);
-        }
-        __syncthreads();
-        if (kb0 + kKeys < k_end) fetch(kb0 + kKeys);
-        uint64_t mword = ~0ull;
-        if (tree) mword = row_ok ? a.plan.mask[(long long)node * a.plan.mask_words + (kb0 >> 6)] : 0ull;
 
+    // One 64-key block: TREE adds the ancestor mask; `whole` blocks of the prefix need no
+    // per-key test at all (rows past the end have zero queries, so their scores stay
+    // finite, and they are never stored).
+    auto block = [&](auto tree_tag, int kb0) {
+        constexpr bool TREE = decltype(tree_tag)::value;
+        const bool whole = kb0 + kKeys <= k_end;
+        const uint64_t mword = TREE && row_ok ? a.plan.mask[(long long)node * a.plan.mask_words + (kb0 >> 6)] : 0ull;
 #pragma unroll
         for (int kb = 0; kb < kKeys; kb += 32) {
             if (kb0 + kb >= k_end) break;
@@ -211,27 +212,28 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int kl = kb + t * 16 + 4 * lg + j;        // key within the block
-                    bool ok = row_ok && kb0 + kl < k_end;
-                    if (tree) ok = ok && ((mword >> kl) & 1ull);
-                    const float v = ok ? sc[t][j] * a.scale_log2 : -INFINITY;
+                    float v = sc[t][j] * a.scale_log2;
+                    if (TREE) {
+                        const bool ok = kb0 + kl < k_end && ((mword >> kl) & 1ull);
+                        v = ok ? v : -INFINITY;
+                    } else if (!whole) {
+                        v = kb0 + kl < k_end ? v : -INFINITY;
+                    }
                     p[t * 4 + j] = v;
                     mx = fmaxf(mx, v);
                 }
             mx = fmaxf(mx, shfl_xor_f(mx, 16));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
             const float m_new = fmaxf(m_run, mx);
-            float alpha = 1.f;
-            if (m_new == -INFINITY) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = 0.f;
-            } else {
-                alpha = exp2f(m_run - m_new);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = exp2f(p[e] - m_new);
-            }
+            // a row with every key of the step masked (only in the tree) keeps p = 0
+            const float m_use = (TREE && m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
             float psum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) psum += p[e];
+            for (int e = 0; e < 8; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(p[e] - m_use);
+                psum += p[e];
+            }
             l_run = l_run * alpha + psum;
             m_run = m_new;
             Frag<T> pf, pf_lo;
@@ -246,6 +248,22 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
                 if (Vt4<T>::kSplit) mma(o[t], vf, pf_lo);
             }
         }
+    };
+
+    fetch(k_begin);
+    for (int kb0 = k_begin; kb0 < k_end; kb0 += kKeys) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            *reinterpret_cast<u32x4*>(Ks + kkey[j] * KP + (koff[j] - kkey[j] * (int)kstride)) = kr[j];
+            const int vc8 = voff[j] - vkey[j] * (int)kstride;      // column piece * EPV
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) Vt[(vc8 + e) * VP + vkey[j]] = Vt4<T>::elem(vr[j], e);
+        }
+        __syncthreads();
+        if (kb0 + kKeys < k_end) fetch(kb0 + kKeys);
+        if (tree) block(std::true_type{}, kb0);
+        else block(std::false_type{}, kb0);
     }
     l_run += shfl_xor_f(l_run, 16);
     l_run += shfl_xor_f(l_run, 32);

@@ -18,11 +18,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (inputs here are finite).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest, ties to even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t b = __float_as_uint(f);
-    b += 0x7FFFu + ((b >> 16) & 1u);
-    return static_cast<bf16_t>(b >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+// Two values packed as one 32-bit word, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Elem;

@@ -1032,8 +1032,6 @@ __global__ __launch_bounds__(kThreads) void splitk_finalize_kernel(const GemmBat
 // partial sums are reduced across the wave in a fixed order.  Results go to LDS and the
 // same epilogues as the MFMA kernels run on them (per-tile top-s, or bias/SiLU/residual
 // store), with the same tiles (128 rows for top-s, 32 for the store).
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ float dot8(const u32x4& w, const u32x4& x, float acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
