@@ -27,7 +27,7 @@ DOMINANT = "heads_vocab"        # the kernel with most of the step's bytes (A2+A
 # the sources it was measured on are unchanged (their hash is recorded beside the figure)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "heads_vocab_8b_traffic.md")
 KERNEL_SOURCES = ("speculative_decoding_amd/csrc/gemm.hip", "speculative_decoding_amd/csrc/common.hpp",
-                  "speculative_decoding_amd/csrc/internal.hpp")
+                  "speculative_decoding_amd/csrc/internal.hpp", "speculative_decoding_amd/build.py")
 METRIC = "Medusa verify steps/s + tokens/s and achieved HBM GB/s at 8B shape, 1 GPU"
 
 WORKLOADS = {

@@ -24,7 +24,17 @@ namespace medusa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;     // the combine kernel
+#ifndef MEDUSA_ATTN_WAVES
+#define MEDUSA_ATTN_WAVES 4
+#endif
+// Waves (16 query rows each) per attention workgroup: the K/V blocks staged in LDS are
+// shared by all of them, so more waves mean fewer passes of the same keys through each CU.
+// Measured: 8 waves help at 512 and more query rows per kv head (dense 256-node tree 105 ->
+// 102 us, batched 70B 316 -> 300 us) and cost 3 us at 256 (the 8B tree: 22.5 -> 25.5 us).
+constexpr int kAttnWaves = MEDUSA_ATTN_WAVES;
+constexpr int kAttnRows = 16 * kAttnWaves;
+constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kKeys = 64;          // keys staged per LDS block
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -84,7 +94,7 @@ template <> struct Vt4<float> {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(const AttnArgs a) {
     constexpr int EPV = 16 / sizeof(T);
     constexpr int KP = D + 8;          // K row pitch (elements)
     constexpr int VP = kKeys + 8;      // V^T row pitch
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
     const int lane = threadIdx.x & 63;
     const int ln = lane & 15;
     const int lg = lane >> 4;
-    const int r = qb * 64 + wave * 16 + ln;          // this lane's query row
+    const int r = qb * kAttnRows + wave * 16 + ln;   // this lane's query row
     const bool row_ok = r < sh.rows;
     const int node = row_ok ? r / sh.G : 0;
     const int head = g * sh.G + (row_ok ? r % sh.G : 0);
@@ -148,7 +158,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
     // K/V blocks are fetched into registers one block ahead, so the global loads of block
     // j+1 are in flight while block j is multiplied out of LDS.
     constexpr int VPR = D / EPV;                 // 16-byte vectors per key row
-    constexpr int NV = kKeys * VPR / kThreads;   // vectors per thread per block
+    constexpr int NV = kKeys * VPR / kAttnThreads;   // vectors per thread per block
+    static_assert(NV * kAttnThreads == kKeys * VPR, "K/V block split over the threads");
     // K: consecutive threads read consecutive 16-byte pieces of a key row (coalesced, and
     // stored row-major).  V: consecutive threads take consecutive keys of one 16-byte column
     // piece, so the transposed scalar LDS stores of a wave hit 64 consecutive keys of one
@@ -156,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const AttnArgs a
     int kkey[NV], koff[NV], vkey[NV], voff[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const int idx = threadIdx.x + j * kThreads;
+        const int idx = threadIdx.x + j * kAttnThreads;
         kkey[j] = idx / VPR;
         koff[j] = kkey[j] * (int)kstride + (idx - kkey[j] * VPR) * EPV;
         vkey[j] = idx % kKeys;
@@ -351,7 +362,7 @@ hipError_t launch_td(const AttnArgs& a, hipStream_t stream) {
     const AttnShape& s = a.s;
     const int nblocks = s.B * s.Hkv * (s.n_splits + 1) * s.n_qblocks;
     prof_begin("attn_partial", stream);
-    hipLaunchKernelGGL((attn_partial_kernel<T, D>), dim3(nblocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_kernel<T, D>), dim3(nblocks), dim3(kAttnThreads), 0, stream, a);
     prof_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -369,14 +380,15 @@ AttnShape attn_shape(int B, int N, int Hq, int Hkv, int d, int Lcap) {
     s.B = B; s.N = N; s.Hq = Hq; s.Hkv = Hkv; s.d = d; s.Lcap = Lcap;
     s.G = Hq / Hkv;
     s.rows = N * s.G;
-    s.n_qblocks = (s.rows + 63) / 64;
+    s.n_qblocks = (s.rows + kAttnRows - 1) / kAttnRows;
     // Split the prefix so that (a) the partial outputs (rows * d fp32 per split) stay
     // below about half the K/V bytes they summarise and (b) the grid still covers the
     // chip when there are few (sequence, kv head, query block) triples.
     const int max_splits = Lcap > 0 ? (Lcap + kKeys - 1) / kKeys : 1;
     int splits = Lcap / (2 * s.rows);
     const int base = B * Hkv * s.n_qblocks;
-    const int fill = (512 + base - 1) / base;
+    const int fill_blocks = 2048 / kAttnWaves;        // about 2048 waves in flight
+    const int fill = (fill_blocks + base - 1) / base;
     if (splits < fill) splits = fill;
     if (splits < 1) splits = 1;
     if (splits > max_splits) splits = max_splits;
