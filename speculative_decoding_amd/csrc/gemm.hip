@@ -958,6 +958,189 @@ __global__ __launch_bounds__(NW * kWave) void gemm_cu_partial_kernel(const GemmB
     }
 }
 
+// lm_head over the tree nodes (argmax epilogue), one workgroup per CU.  NW waves of 16*RT
+// weight rows each stream the full contraction through a register ring of PF chunks and a
+// wave-private LDS transpose.  The (up to 64) input rows are staged in LDS one slab of
+// 512 columns at a time, with the next slab held in registers meanwhile.  So the
+// workgroup synchronises twice per eight 64-column chunks instead of twice per chunk, and
+// every CU reads the input rows once instead of once per workgroup.
+constexpr int kSlab = 512;
+
+size_t slab_argmax_lds(int nw, int rt) {
+    return (size_t)64 * (kSlab + 8) * 2 + (size_t)nw * 16 * rt * (64 + 8) * 2 + (size_t)nw * 64 * 8;
+}
+
+template <int NW, int RT, int PF>
+__global__ __launch_bounds__(NW * kWave) void gemm_slab_argmax_kernel(const GemmBatch bt) {
+    constexpr int MT = 4;
+    constexpr int CH = 64;
+    constexpr int ROWS = 16 * RT;
+    constexpr int NWG = NW * ROWS;
+    constexpr int XP = CH + 8;
+    constexpr int LPR = CH / 8;
+    constexpr int RPI = kWave / LPR;
+    constexpr int NI = ROWS / RPI;
+    constexpr int KS = CH / 32;
+    constexpr int SP = kSlab + 8;
+    constexpr int NT = NW * kWave;
+    constexpr int SV = MT * 16 * (kSlab / 8) / NT;     // slab vectors per thread
+    constexpr int CPS = kSlab / CH;                    // chunks per slab
+    static_assert(SV * NT == MT * 16 * (kSlab / 8), "slab split over the threads");
+    static_assert(CPS % PF == 0, "ring slots repeat within a slab");
+    extern __shared__ __align__(16) unsigned char dyn_slab[];
+    bf16_t* xs = reinterpret_cast<bf16_t*>(dyn_slab);                       // [64][SP]
+    bf16_t* wt = xs + MT * 16 * SP;                                         // [NW][ROWS*XP]
+    auto& red_v = *reinterpret_cast<float (*)[NW][MT * 16]>(wt + NW * ROWS * XP);
+    auto& red_i = *reinterpret_cast<int (*)[NW][MT * 16]>(&red_v[NW][0]);
+
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    const int nblocks = bt.total_tiles * n_mb;
+    const int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int mb = bid % n_mb;
+    const int t = bid / n_mb;
+    const GemmProblem& P = bt.p[problem_of(bt, t)];
+    const int tile = t - P.tile_begin;
+    const int K = bt.K;
+    const int N = P.N;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int n_wave = tile * NWG + wave * ROWS;
+    const int m0 = mb * MT * 16;
+    const int Mb = min(bt.M - m0, MT * 16);
+    const int n_ch = K / CH;
+    const int n_slabs = K / kSlab;
+
+    // input slab vectors of this thread: rows without a source read row 0, zeroed on store
+    const bf16_t* X = static_cast<const bf16_t*>(P.X);
+    const bf16_t* xsrc[SV];
+    bool xok[SV];
+    int xdst[SV];
+#pragma unroll
+    for (int j = 0; j < SV; ++j) {
+        const int idx = threadIdx.x + j * NT;
+        const int m = idx / (kSlab / 8);
+        const int c = idx - m * (kSlab / 8);
+        long long r = 0;
+        bool ok = m < Mb;
+        if (ok) {
+            r = m0 + m;
+            if (P.x_rows) {
+                r = P.x_rows[m0 + m];
+                ok = r >= 0 && r < bt.x_rows_bound;
+                if (!ok) r = 0;
+            }
+        }
+        xok[j] = ok;
+        xsrc[j] = X + r * P.x_stride + c * 8;
+        xdst[j] = m * SP + c * 8;
+    }
+    u32x4 xv[SV];
+    auto slab_load = [&](int sl) {
+        const int ks = min(sl, n_slabs - 1) * kSlab;
+#pragma unroll
+        for (int j = 0; j < SV; ++j) xv[j] = *reinterpret_cast<const u32x4*>(xsrc[j] + ks);
+    };
+    auto slab_store = [&]() {
+#pragma unroll
+        for (int j = 0; j < SV; ++j)
+            *reinterpret_cast<u32x4*>(xs + xdst[j]) = xok[j] ? xv[j] : u32x4{0u, 0u, 0u, 0u};
+    };
+
+    const bf16_t* W = static_cast<const bf16_t*>(P.W);
+    const int half = lane / LPR;
+    const int col = (lane % LPR) * 8;
+    const u32x4* wsrc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int n = min(n_wave + RPI * i + half, N - 1);
+        wsrc[i] = reinterpret_cast<const u32x4*>(W + (long long)n * K + col);
+    }
+    u32x4 wr[PF][NI];
+    auto load_w = [&](int q, int c) {
+        const int kc = min(c, n_ch - 1) * CH;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) wr[q][i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
+    };
+    bf16_t* wtile = wt + wave * ROWS * XP;
+
+    floatx4 acc[RT][MT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int q = 0; q < PF; ++q) load_w(q, q);
+    slab_load(0);
+    slab_store();
+    slab_load(1);
+    __syncthreads();
+    for (int c0 = 0; c0 < n_ch; c0 += CPS) {
+        if (c0 > 0) {
+            // every wave is done with the previous slab: replace it with the prefetched one
+            __syncthreads();
+            slab_store();
+            __syncthreads();
+            slab_load(c0 / CPS + 1);
+        }
+#pragma unroll
+        for (int u = 0; u < CPS; ++u) {
+            const int c = c0 + u;
+            const int q = u % PF;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                *reinterpret_cast<u32x4*>(wtile + (RPI * i + half) * XP + col) = wr[q][i];
+            load_w(q, c + PF);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Frag<bf16_t> wf[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) wf[rt].load(wtile + (rt * 16 + ln) * XP + 32 * ks + 8 * lg);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    Frag<bf16_t> xf;
+                    xf.load(xs + (mt * 16 + ln) * SP + u * CH + 32 * ks + 8 * lg);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) mma(acc[rt][mt], xf, wf[rt]);
+                }
+            }
+            // the next chunk's transpose reuses this wave's tile: order the reads before it
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+    __syncthreads();
+    tile_epilogue<MT, RT, NWG, EPI_ARGMAX, NW>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane,
+                                               nullptr, red_v, red_i);
+}
+
+#ifndef MEDUSA_SLAB_NW
+#define MEDUSA_SLAB_NW 8
+#endif
+#ifndef MEDUSA_SLAB_RT
+#define MEDUSA_SLAB_RT 4
+#endif
+#ifndef MEDUSA_SLAB_PF
+#define MEDUSA_SLAB_PF 2
+#endif
+#ifndef MEDUSA_SLAB
+#define MEDUSA_SLAB 1
+#endif
+constexpr int kSlabNw = MEDUSA_SLAB_NW;
+constexpr int kSlabRt = MEDUSA_SLAB_RT;
+constexpr int kSlabPf = MEDUSA_SLAB_PF;
+
+// The slab argmax kernel: bf16, contraction a multiple of the 512-column slab, more than
+// 64 input rows.  Measured in the step: dense 256-node tree (256 rows) 472 -> 413 us against
+// the row-streaming kernel; at 64 rows two row-streaming workgroups per CU hide latency
+// better (170 against 176 us).
+__host__ bool slab_argmax_eligible(medusa_dtype dt, int epi, int M, int K) {
+    return MEDUSA_SLAB && dt == MEDUSA_BF16 && epi == EPI_ARGMAX && M > 64 && K % kSlab == 0;
+}
+
 // Sum the contraction slices of every (m, n) in slice order and apply the store epilogue:
 // out[m][n] = rnd(silu?(sum + bias[n]) + residual[m][n]).  Four consecutive n per thread.
 template <typename T>
@@ -1379,6 +1562,7 @@ bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
 int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
     if (epi == EPI_PARTIAL) return kWavePartialRows;
+    if (slab_argmax_eligible(dt, epi, M, K)) return kSlabNw * 16 * kSlabRt;
     if (rowstream_eligible(dt, epi, M, K))
         return epi == EPI_ARGMAX ? kRsWavesArgmax * 16 * kRsRtwArgmax : kWaves * 16 * kRsRtw;
     int rt;
@@ -1445,6 +1629,21 @@ hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
     if (epi == EPI_TOPS)
         return launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunk, kWaves>(bt, stream);
     return launch_rowstream_m<EPI_ARGMAX, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
+}
+
+hipError_t launch_slab_argmax(GemmBatch& bt, hipStream_t stream) {
+    auto kern = gemm_slab_argmax_kernel<kSlabNw, kSlabRt, kSlabPf>;
+    const size_t lds = slab_argmax_lds(kSlabNw, kSlabRt);
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int n_mb = (bt.M + 63) / 64;
+    hipLaunchKernelGGL(kern, dim3(bt.total_tiles * n_mb), dim3(kSlabNw * kWave), lds, stream, bt);
+    return hipGetLastError();
 }
 
 // Row-streaming MFMA path: bf16, contraction a multiple of its 256-wide chunk, argmax or
@@ -1568,6 +1767,7 @@ hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& bt, hipStream_t
 }
 
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& bt, hipStream_t stream) {
+    if (slab_argmax_eligible(dt, epi, bt.M, bt.K)) return launch_slab_argmax(bt, stream);
     if (rowstream_eligible(dt, epi, bt.M, bt.K)) return launch_rowstream(epi, bt, stream);
     if (gemv_eligible(dt, epi, bt))
         return epi == EPI_TOPS ? launch_gemv_k<EPI_TOPS>(bt, stream) : launch_gemv_k<EPI_STORE>(bt, stream);

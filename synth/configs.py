@@ -122,6 +122,13 @@ CONFIGS = {
         tree_s=(4, 3, 2), n_nodes=16, Hq=4, Hkv=1, d=64, lens=(0, 129, 300), Lcap=300,
         sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
         sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
+    # a full 4x4x4 tree (85 nodes) for two sequences: 170 verified rows, more than one
+    # 64-row block of the lm_head kernels, the last one ragged
+    "small_dense": Config(
+        name="small_dense", B=2, H=512, V=2003, K=3, s=(4, 4, 4), tree="full",
+        tree_s=(4, 4, 4), n_nodes=85, Hq=4, Hkv=2, d=64, lens=(100, 257), Lcap=260,
+        sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
+        sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
 }
 
 
