@@ -33,6 +33,11 @@ Steps and the passages they follow:
   argmax is emitted after it (the blog page "Medusa no contexto de LLMs",
   section "o que significa medusa na prática de deploy": on rejection, fall
   back to the conventionally generated token).
+* ``advance``, ``decode_loop`` — the next round: the longest accepted branch is
+  kept and its last hidden state feeds the heads (glossary, section "Attention
+  arborescente et acceptation").  The branch's rows join the KV cache, the
+  deepest accepted node's hidden state becomes the next h and its argmax (the
+  emitted bonus token) the next root.
 * ``greedy_decode``   — the definition the step must reproduce: plain
   step-by-step greedy decoding with the same verifier ("Medusa Decoding
   Heads", section "Diepe duik": accepted text is exactly what greedy decoding
@@ -50,7 +55,8 @@ from .plan_ref import TreePlan
 __all__ = [
     "as_f64", "round_act", "silu", "matvec_rows", "heads_forward", "lm_head_logits", "topk",
     "argmax_lowest", "build_tree", "proxy_qkv", "tree_attention", "proxy_out", "verify",
-    "accept", "greedy_decode", "StepResult", "step", "causal_attention_last",
+    "accept", "greedy_decode", "StepResult", "step", "causal_attention_last", "store_act",
+    "advance", "decode_loop",
 ]
 
 _CHUNK_ROWS = 8192
@@ -382,3 +388,77 @@ def step(inp, plan: TreePlan, root: Optional[np.ndarray] = None) -> StepResult:
                       topk_vals=vals, u=u, tokens=tokens, pos=pos, x=x, q=q, k=k, v=v, o=o,
                       node_hidden=nh, logits=logits, node_argmax=am, accept_len=alen,
                       accept_nodes=anodes, accept_tokens=atoks)
+
+
+# ----------------------------------------------------------------- the next round
+
+def store_act(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage form of activation values that are already rounded to ``dtype``: bf16 bit
+    patterns (uint16) or float32.  Exact: every input value is representable."""
+    if dtype == "bf16":
+        f = np.asarray(x, dtype=np.float64).astype(np.float32)
+        if not np.array_equal(f.astype(np.float64), np.asarray(x, dtype=np.float64)):
+            raise ValueError("value not representable in fp32")
+        bits = f.view(np.uint32)
+        if np.any(bits & np.uint32(0xFFFF)):
+            raise ValueError("value not representable in bf16")
+        return (bits >> np.uint32(16)).astype(np.uint16)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32)
+    raise ValueError(dtype)
+
+
+def advance(inp, plan: TreePlan, res: StepResult):
+    """Commit one step's accepted branch and set up the next round.
+
+    For sequence b with a = accept_len[b] and path = accept_nodes[b, :a+1] (root
+    first): the tree K/V rows of the path become KV-cache rows L_b .. L_b + a (they
+    are the keys and values greedy decoding computes for those tokens), L_b grows by
+    a + 1, the next last hidden state is node_hidden at the path's deepest node, and
+    the next root is the emitted bonus token accept_tokens[b, a].
+
+    Returns (inputs for the next step, next roots [B]).  ``inp`` is not modified.
+    Raises ValueError when a branch does not fit in the cache (L_b + a + 1 > Lcap)."""
+    import copy
+    cfg = inp.cfg
+    dt = inp.dtype
+    nxt = copy.copy(inp)
+    nxt.k_cache = inp.k_cache.copy()
+    nxt.v_cache = inp.v_cache.copy()
+    nxt.prefix_lens = inp.prefix_lens.copy()
+    nxt.h = inp.h.copy()
+    roots = np.empty(cfg.B, dtype=np.int64)
+    for b in range(cfg.B):
+        L = int(inp.prefix_lens[b])
+        a = int(res.accept_len[b])
+        path = [int(i) for i in res.accept_nodes[b, : a + 1]]
+        if L + a + 1 > cfg.Lcap:
+            raise ValueError(f"sequence {b}: {a + 1} rows do not fit after {L} of {cfg.Lcap}")
+        nxt.k_cache[b, L: L + a + 1] = store_act(res.k[b, path], dt)
+        nxt.v_cache[b, L: L + a + 1] = store_act(res.v[b, path], dt)
+        nxt.prefix_lens[b] = L + a + 1
+        nxt.h[b] = store_act(res.node_hidden[b, path[a]], dt)
+        roots[b] = int(res.accept_tokens[b, a])
+    return nxt, roots
+
+
+def decode_loop(inp, plan: TreePlan, steps: int):
+    """``steps`` whole Medusa steps, each followed by ``advance``; the first bootstraps
+    its root as argmax(lm_head(h)).
+
+    Returns (first roots [B], emitted streams: one int64 array per sequence holding
+    every step's accepted candidates and bonus token, per-step StepResults)."""
+    cur = inp
+    root = None
+    results = []
+    streams = [[] for _ in range(inp.cfg.B)]
+    for _ in range(steps):
+        res = step(cur, plan, root)
+        results.append(res)
+        for b in range(inp.cfg.B):
+            a = int(res.accept_len[b])
+            streams[b].extend(int(t) for t in res.accept_tokens[b, : a + 1])
+        cur, root = advance(cur, plan, res)
+    return (np.asarray(results[0].root, dtype=np.int64),
+            [np.array(t, dtype=np.int64) for t in streams], results)
+

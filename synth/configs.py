@@ -129,6 +129,17 @@ CONFIGS = {
         tree_s=(4, 4, 4), n_nodes=85, Hq=4, Hkv=2, d=64, lens=(100, 257), Lcap=260,
         sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
         sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
+    # decode-loop cases: room in the KV cache for several rounds of accepted branches
+    "tiny_loop": Config(
+        name="tiny_loop", B=1, H=256, V=1000, K=3, s=(2, 3, 3), tree="full", tree_s=(2, 3),
+        n_nodes=9, Hq=4, Hkv=4, d=64, L=32, Lcap=64, dtype="f32",
+        sigma_lm=_inv_sqrt(256), sigma_w1=_inv_sqrt(256), sigma_b1=_inv_sqrt(256),
+        sigma_w2=_inv_sqrt(256), sigma_proxy=_inv_sqrt(256)),
+    "small_loop": Config(
+        name="small_loop", B=2, H=512, V=3001, K=3, s=(4, 3, 2), tree="sparse",
+        tree_s=(4, 3, 2), n_nodes=16, Hq=4, Hkv=2, d=64, lens=(40, 97), Lcap=160,
+        sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
+        sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
 }
 
 

@@ -338,3 +338,47 @@ def test_step_equals_greedy_decoding(cfg, seed):
             node = int(res.accept_nodes[b, a])
             kids = [i for i in range(plan.n_nodes) if plan.parent[i] == node]
             assert int(g[a]) not in {int(res.tokens[b, i]) for i in kids}
+
+
+@pytest.mark.parametrize("cfg,seed", [("tiny_loop", 0), ("tiny_loop", 2), ("small_loop", 1),
+                                      ("small_loop", 3)])
+def test_decode_loop_equals_greedy_decoding(cfg, seed):
+    """Several rounds, each keeping the longest accepted branch and feeding its last
+    hidden state to the heads (glossary "Medusa Heads", section "Attention arborescente
+    et acceptation"), emit exactly the plain greedy stream ("Medusa Decoding Heads",
+    section "Diepe duik"), and the cache holds the rows greedy decoding would have
+    appended."""
+    from tests import planting
+    inp = planting.planted_inputs(cfg, seed)
+    plan = planting.plan_for(inp.cfg, inp.acc)
+    root0, streams, res = oracle.decode_loop(inp, plan, 4)
+    assert any(int(r.accept_len.max()) > 0 for r in res)      # some branch longer than the root
+    for b in range(inp.cfg.B):
+        g, _, _ = oracle.greedy_decode(inp, b, int(root0[b]), len(streams[b]))
+        assert streams[b].tolist() == g.tolist()
+    # the cache after the rounds: prefix unchanged, then the root and each round's accepted
+    # tokens, with the k/v the verifier computes for them
+    cur, root = inp, None
+    for r in res:
+        cur_next, root = oracle.advance(cur, plan, r)
+        for b in range(inp.cfg.B):
+            L, a = int(cur.prefix_lens[b]), int(r.accept_len[b])
+            assert int(cur_next.prefix_lens[b]) == L + a + 1
+            assert np.array_equal(cur_next.k_cache[b, :L], cur.k_cache[b, :L])   # earlier rows kept
+            assert np.array_equal(cur_next.v_cache[b, :L], cur.v_cache[b, :L])
+            toks = [int(r.tokens[b, 0])] + [int(t) for t in r.accept_tokens[b, :a]]
+            _, _, k_ref, v_ref = oracle.proxy_qkv(np.array([toks]), inp.embed, inp.wq, inp.wk, inp.wv,
+                                                  inp.cfg.Hq, inp.cfg.Hkv, inp.cfg.d, inp.dtype)
+            got_k = oracle.as_f64(cur_next.k_cache[b, L: L + a + 1], inp.dtype)
+            got_v = oracle.as_f64(cur_next.v_cache[b, L: L + a + 1], inp.dtype)
+            assert np.array_equal(got_k, k_ref[0]) and np.array_equal(got_v, v_ref[0])
+        cur = cur_next
+
+
+def test_advance_rejects_a_full_cache():
+    from tests import planting
+    inp = planting.planted_inputs("tiny", 0)       # Lcap == L: no room for the root's row
+    plan = planting.plan_for(inp.cfg, inp.acc)
+    res = oracle.step(inp, plan)
+    with pytest.raises(ValueError):
+        oracle.advance(inp, plan, res)
