@@ -189,6 +189,31 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
                                    size_t ws_bytes, void* stream);
 size_t medusa_verify_workspace(const medusa_tree_plan* plan, medusa_dtype dt, int B, int H, int V);
 
+/* ------------------------------------------------------------------ 5. next round
+ * Commit each sequence's accepted branch and set up the next step (glossary, "Attention
+ * arborescente et acceptation": the longest accepted branch is kept and its last hidden
+ * state feeds the heads in the next round).  With a = accept_len[b], the branch
+ * accept_nodes[b, 0..a] (root first) and L = prefix_lens[b]:
+ *     k_cache[b, L + j] = k_tree[b, accept_nodes[b, j]],  v likewise,   j = 0..a
+ *     prefix_lens[b] = L + a + 1
+ *     hidden_out[b] = node_hidden[b, accept_nodes[b, a]]   (the next step's h)
+ *     root_out[b]   = accept_tokens[b, a]                  (the next step's root: the bonus)
+ * These are exactly the cache rows and the state plain greedy decoding reaches after the
+ * emitted tokens.  A branch that does not fit (L + a + 1 > Lcap) changes nothing for its
+ * sequence and sets overflow[b] = 1 (0 otherwise) when overflow is not NULL.
+ *   accept_len [B], accept_nodes, accept_tokens [B, D+1] int32 (as written by
+ *   medusa_verify_accept; D = the plan's depth)   k_tree, v_tree [B,N,Hkv,d] dtype
+ *   node_hidden [B,N,H] dtype   k_cache, v_cache [B,Lcap,Hkv,d] and prefix_lens [B] int32,
+ *   updated in place   hidden_out [B,H] dtype (typically the h buffer the next
+ *   medusa_heads_forward reads; must not overlap node_hidden)   root_out [B] int32
+ *   overflow [B] int32 or NULL.   (Hkv*d) % 8 == 0 and H % 8 == 0; 16-byte aligned rows. */
+medusa_status medusa_advance(const medusa_tree_plan* plan, medusa_dtype dt, int B, int H, int Hkv,
+                             int d, int Lcap, const int32_t* accept_len,
+                             const int32_t* accept_nodes, const int32_t* accept_tokens,
+                             const void* k_tree, const void* v_tree, const void* node_hidden,
+                             void* k_cache, void* v_cache, int32_t* prefix_lens, void* hidden_out,
+                             int32_t* root_out, int32_t* overflow, void* stream);
+
 /* ------------------------------------------------------------------ one-layer verifier
  * A stand-in for the frozen base model that scores the tree (not part of the method):
  * embedding gather, Q/K/V projections, and the attention output projection with the

@@ -47,6 +47,9 @@ _SIGS = {
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_size_t, c_void_p]),
     "medusa_verify_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int, c_int]),
+    "medusa_advance": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "medusa_proxy_workspace": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "medusa_proxy_qkv": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

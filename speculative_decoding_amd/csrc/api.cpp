@@ -350,6 +350,60 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
     return MEDUSA_OK;
 }
 
+// ------------------------------------------------------------------ next round
+
+medusa_status medusa_advance(const medusa_tree_plan* plan, medusa_dtype dt, int B, int H, int Hkv,
+                             int d, int Lcap, const int32_t* accept_len,
+                             const int32_t* accept_nodes, const int32_t* accept_tokens,
+                             const void* k_tree, const void* v_tree, const void* node_hidden,
+                             void* k_cache, void* v_cache, int32_t* prefix_lens, void* hidden_out,
+                             int32_t* root_out, int32_t* overflow, void* stream) {
+    if (!plan || !accept_len || !accept_nodes || !accept_tokens || !k_tree || !v_tree ||
+        !node_hidden || !k_cache || !v_cache || !prefix_lens || !hidden_out || !root_out)
+        return MEDUSA_ERR_NULL;
+    if (!dtype_ok(dt)) return MEDUSA_ERR_UNSUPPORTED;
+    const size_t es = esize(dt);
+    if (B < 1 || B > 4096 || H < 1 || Hkv < 1 || d < 1 || Lcap < 1 || Lcap > (1 << 20))
+        return MEDUSA_ERR_SHAPE;
+    const size_t row_bytes = (size_t)Hkv * d * es;
+    const size_t hidden_bytes = (size_t)H * es;
+    if (row_bytes % 16 != 0 || hidden_bytes % 16 != 0) return MEDUSA_ERR_SHAPE;
+    if (!aligned16(k_tree) || !aligned16(v_tree) || !aligned16(node_hidden) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(hidden_out))
+        return MEDUSA_ERR_SHAPE;
+    const int N = plan->n_nodes;
+    // hidden_out is written while node_hidden is read
+    const uintptr_t h0 = reinterpret_cast<uintptr_t>(hidden_out), h1 = h0 + (size_t)B * hidden_bytes;
+    const uintptr_t n0 = reinterpret_cast<uintptr_t>(node_hidden), n1 = n0 + (size_t)B * N * hidden_bytes;
+    if (h0 < n1 && n0 < h1) return MEDUSA_ERR_SHAPE;
+    medusa_status st = medusa_internal_device_check();
+    if (st != MEDUSA_OK) return st;
+    AdvanceArgs a{};
+    a.accept_len = accept_len;
+    a.accept_nodes = accept_nodes;
+    a.accept_tokens = accept_tokens;
+    a.k_tree = k_tree;
+    a.v_tree = v_tree;
+    a.node_hidden = node_hidden;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.prefix_lens = prefix_lens;
+    a.hidden_out = hidden_out;
+    a.root_out = root_out;
+    a.overflow = overflow;
+    a.n_nodes = N;
+    a.max_depth = plan->max_depth;
+    a.Lcap = Lcap;
+    a.row_bytes = (int)row_bytes;
+    a.hidden_bytes = (int)hidden_bytes;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    prof_begin("advance", strm);
+    const hipError_t e = advance_launch(a, B, strm);
+    prof_end(strm);
+    if (e != hipSuccess) return medusa_internal_hip_error(e);
+    return MEDUSA_OK;
+}
+
 // ------------------------------------------------------------------ one-layer verifier
 
 namespace {

@@ -114,7 +114,53 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     }
 }
 
+// Next round (same section: the longest accepted branch is kept and its last hidden state
+// feeds the heads next time): the branch's tree K/V rows join the cache after the prefix,
+// the deepest accepted node's hidden state and bonus token become the next h and root.
+// One workgroup per sequence; every row moves as 16-byte vectors.  All threads read the
+// old length before thread 0 replaces it.
+__global__ __launch_bounds__(256) void advance_kernel(AdvanceArgs a) {
+    const int b = blockIdx.x;
+    const int D1 = a.max_depth + 1;
+    const int L = a.prefix_lens[b];
+    const int acc = min(max(a.accept_len[b], 0), a.max_depth);
+    const bool fits = L >= 0 && L + acc + 1 <= a.Lcap;
+    const int32_t* nodes = a.accept_nodes + (long long)b * D1;
+    auto node_at = [&](int j) { return min(max(nodes[j], 0), a.n_nodes - 1); };
+    if (fits) {
+        const int vpr = a.row_bytes / 16;                     // vectors per K/V row
+        const int total = (acc + 1) * vpr;
+        for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+            const int j = idx / vpr;
+            const int c = idx - j * vpr;
+            const long long src = ((long long)b * a.n_nodes + node_at(j)) * vpr + c;
+            const long long dst = ((long long)b * a.Lcap + L + j) * vpr + c;
+            reinterpret_cast<u32x4*>(a.k_cache)[dst] = reinterpret_cast<const u32x4*>(a.k_tree)[src];
+            reinterpret_cast<u32x4*>(a.v_cache)[dst] = reinterpret_cast<const u32x4*>(a.v_tree)[src];
+        }
+        const int hv = a.hidden_bytes / 16;
+        const long long hsrc = ((long long)b * a.n_nodes + node_at(acc)) * hv;
+        for (int c = threadIdx.x; c < hv; c += blockDim.x)
+            reinterpret_cast<u32x4*>(a.hidden_out)[(long long)b * hv + c] =
+                reinterpret_cast<const u32x4*>(a.node_hidden)[hsrc + c];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (fits) {
+            a.prefix_lens[b] = L + acc + 1;
+            a.root_out[b] = a.accept_tokens[(long long)b * D1 + acc];
+        }
+        if (a.overflow) a.overflow[b] = fits ? 0 : 1;
+    }
+}
+
 }  // namespace
+
+hipError_t advance_launch(const AdvanceArgs& args, int B, hipStream_t stream) {
+    hipLaunchKernelGGL(advance_kernel, dim3(B), dim3(256), 0, stream, args);
+    return hipGetLastError();
+}
+
 
 hipError_t build_tree_launch(const DevicePlan& plan, int B, int K, int s_max,
                              const int32_t* root_ids, const int32_t* topk_ids,

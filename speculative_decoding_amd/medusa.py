@@ -219,6 +219,22 @@ def medusa_verify_workspace(plan: TreePlan, dt, B, H, V) -> int:
     return int(lib().medusa_verify_workspace(plan.handle, _dt(dt), B, H, V))
 
 
+def medusa_advance(plan: TreePlan, dt, B, H, Hkv, d, Lcap, accept_len, accept_nodes,
+                   accept_tokens, k_tree, v_tree, node_hidden, k_cache, v_cache, prefix_lens,
+                   hidden_out, root_out, overflow=None, stream=None):
+    torch = _torch()
+    st = lib().medusa_advance(
+        plan.handle, _dt(dt), B, H, Hkv, d, Lcap, _ptr(accept_len, torch.int32, "accept_len"),
+        _ptr(accept_nodes, torch.int32, "accept_nodes"),
+        _ptr(accept_tokens, torch.int32, "accept_tokens"), _float_ptr(k_tree, dt, "k_tree"),
+        _float_ptr(v_tree, dt, "v_tree"), _float_ptr(node_hidden, dt, "node_hidden"),
+        _float_ptr(k_cache, dt, "k_cache"), _float_ptr(v_cache, dt, "v_cache"),
+        _ptr(prefix_lens, torch.int32, "prefix_lens"), _float_ptr(hidden_out, dt, "hidden_out"),
+        _ptr(root_out, torch.int32, "root_out"), _ptr(overflow, torch.int32, "overflow"),
+        _stream(stream))
+    _check("medusa_advance", st)
+
+
 def medusa_verify_accept(plan: TreePlan, dt, B, H, V, node_hidden, w_lm, node_tokens,
                          node_argmax, accept_len, accept_nodes, accept_tokens, logits=None,
                          ws=None, stream=None):

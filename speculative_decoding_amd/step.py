@@ -135,6 +135,46 @@ class MedusaStep:
                                self.accept_nodes, self.accept_tokens, self.verify_logits,
                                self.ws_verify)
 
+    def advance(self, overflow=None):
+        """Commit the accepted branches: their tree K/V rows join w["k_cache"]/w["v_cache"]
+        after the prefix, w["prefix_lens"] grows, w["h"] becomes the deepest accepted
+        node's hidden state and root_ids the bonus token, so the next run() is the next
+        round.  The weights dict's cache, lengths and h are updated in place."""
+        d, w = self.dims, self.w
+        M.medusa_advance(self.plan, d.dtype, d.B, d.H, d.Hkv, d.d, d.Lcap, self.accept_len,
+                         self.accept_nodes, self.accept_tokens, self.k_tree, self.v_tree,
+                         self.node_hidden, w["k_cache"], w["v_cache"], w["prefix_lens"], w["h"],
+                         self.root_ids, overflow)
+
+    def decode(self, steps: int, bootstrap_root: bool = True):
+        """``steps`` rounds of run() + advance(), all enqueued without a host
+        synchronisation.  Returns device tensors: the first roots [B], and per round the
+        accepted lengths [steps, B], emitted tokens [steps, B, D+1] (accepted candidates
+        then the bonus) and overflow flags [steps, B]."""
+        torch = _torch()
+        B, D = self.dims.B, self.D
+        dev = self.accept_len.device
+        lens = torch.empty(steps, B, dtype=torch.int32, device=dev)
+        toks = torch.empty(steps, B, D + 1, dtype=torch.int32, device=dev)
+        over = torch.empty(steps, B, dtype=torch.int32, device=dev)
+        root0 = None
+        for i in range(steps):
+            self.run(bootstrap_root=bootstrap_root and i == 0, keep_u=False)
+            if i == 0:
+                root0 = self.root_ids.clone()
+            lens[i].copy_(self.accept_len)
+            toks[i].copy_(self.accept_tokens)
+            self.advance(overflow=over[i])
+        return root0, lens, toks, over
+
+    @staticmethod
+    def streams(lens, toks):
+        """Host copy of each sequence's emitted tokens over the rounds of decode()."""
+        lens = lens.cpu().numpy()
+        toks = toks.cpu().numpy()
+        return [np.concatenate([toks[i, b, : lens[i, b] + 1] for i in range(lens.shape[0])]).astype(np.int64)
+                for b in range(lens.shape[1])]
+
     def run(self, bootstrap_root: bool = False, keep_u: bool = True):
         """Enqueue one whole step.  With bootstrap_root the root token is computed as
         argmax(lm_head(h)); otherwise root_ids holds it (the previous step's bonus)."""

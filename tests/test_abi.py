@@ -152,3 +152,25 @@ def test_tree_and_attention_error_paths():
                               FAKE, FAKE, FAKE, 64, None) == 5
     assert M.medusa_proxy_workspace("bf16", 64, 4096, 32, 8, 128) > 1 << 20
     assert L.medusa_status_string(5) == b"workspace too small"
+
+
+def _advance(L, plan, **over):
+    a = dict(dt=1, B=1, H=256, Hkv=4, d=64, Lcap=64, alen=FAKE, anodes=FAKE, atoks=FAKE,
+             kt=FAKE, vt=FAKE, nh=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, hout=FAKE + (1 << 24),
+             root=FAKE, over=None)
+    a.update(over)
+    return L.medusa_advance(plan.handle, a["dt"], a["B"], a["H"], a["Hkv"], a["d"], a["Lcap"],
+                            a["alen"], a["anodes"], a["atoks"], a["kt"], a["vt"], a["nh"], a["kc"],
+                            a["vc"], a["lens"], a["hout"], a["root"], a["over"], None)
+
+
+def test_advance_error_paths():
+    L = lib()
+    plan = M.medusa_tree_plan_full((2, 3))
+    assert _advance(L, plan, alen=None) == 1
+    assert _advance(L, plan, hout=None) == 1
+    assert _advance(L, plan, dt=7) == 3
+    assert _advance(L, plan, d=3) == 2                   # K/V row not a multiple of 16 bytes
+    assert _advance(L, plan, kc=FAKE + 8) == 2           # misaligned
+    assert _advance(L, plan, hout=FAKE) == 2             # next h overlaps node_hidden
+    assert _advance(L, plan, Lcap=0) == 2
