@@ -66,6 +66,44 @@ def algorithmic_bytes(cfg, n_nodes: int, prefix_total: int) -> dict:
     return parts
 
 
+def decode_loop_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, rounds: int):
+    """Rounds of the whole step plus medusa_advance, timed end to end on a copy of the
+    inputs whose KV cache has room for every round (the same weights; the cache rows past
+    the prefix start as zeros and fill with the accepted branches).  Emitted tokens per
+    second count every accepted candidate and bonus token."""
+    if rounds <= 0:
+        return None
+    import dataclasses
+    Lcap = cfg.Lcap + rounds * (plan.max_depth + 1)
+    dims = dataclasses.replace(Dims.from_config(cfg), Lcap=Lcap)
+
+    def fresh():
+        w2 = dict(w)
+        for name in ("k_cache", "v_cache"):
+            t = torch.zeros((cfg.B, Lcap) + tuple(w[name].shape[2:]), dtype=w[name].dtype, device=dev)
+            t[:, : cfg.Lcap] = w[name]
+            w2[name] = t
+        w2["prefix_lens"] = w["prefix_lens"].clone()
+        w2["h"] = w["h"].clone()
+        return MedusaStep(dims, w2, plan, dev)
+
+    fresh().decode(2)                       # warm-up on a throwaway state
+    st = fresh()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, lens, toks, over = st.decode(rounds)
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    streams = st.streams(lens, toks)
+    tokens = int(sum(len(x) for x in streams))
+    return {"rounds": rounds, "emitted_tokens": tokens, "seconds": sec,
+            "rounds_per_s": rounds / sec, "tokens_per_s": tokens / sec,
+            "mean_accept_len": float(lens.float().mean().item()),
+            "overflow": int(over.max().item()),
+            "note": "heads are random apart from the planted first round, so later rounds "
+                    "mostly accept nothing; every round still emits its bonus token"}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -137,6 +175,9 @@ def main() -> int:
     ap.add_argument("--config", default="8b", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--loop-rounds", type=int, default=32,
+                    help="also time this many rounds of the decode loop (step + advance) on a "
+                         "copy of the inputs whose KV cache has room for them (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run an elementwise kernel that reads and writes this many MiB once before "
                          "the timed region (known sizes to calibrate rocprofv3 byte counters)")
@@ -222,6 +263,7 @@ def main() -> int:
             kernels[name] = {"avg_us": 1e3 * ms / n, "launches": n}
 
     res = step.results()
+    loop = decode_loop_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, args.loop_rounds)
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "cus": props.multi_processor_count,
               "arch": getattr(props, "gcnArchName", ""), "hbm_gib": round(props.total_memory / 2**30)}
@@ -271,6 +313,7 @@ def main() -> int:
         "algorithmic_bytes_per_step": ab["total"],
         "roofline": roof,
         "kernels": kernels,
+        "decode_loop": loop,
         "device": device,
         "kernels_note": "per-kernel averages from a second pass of the same steps with every "
                         "launch event-timed (not the timed region)",

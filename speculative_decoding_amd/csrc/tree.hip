@@ -10,6 +10,7 @@
 // node's own first choice is emitted after it.
 #include "common.hpp"
 #include "internal.hpp"
+#include "advance.hpp"
 
 #include <limits.h>
 
