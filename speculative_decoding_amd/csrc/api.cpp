@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "advance.hpp"
 #include "plan_impl.hpp"
 
 using namespace medusa;
