@@ -104,6 +104,55 @@ def decode_loop_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, rounds: int)
                     "mostly accept nothing; every round still emits its bonus token"}
 
 
+SWEEP_DENSE = {4: (3, 4, 4, 4)}     # the dense 256-node tree (1+3+12+48+192) for four heads
+SWEEP_NODES = "1,16,32,64,128,256,341"
+
+
+def node_sweep(torch, M, MedusaStep, Dims, cfg, w, dev, seed: int, node_counts, steps: int,
+               warmup: int):
+    """Whole-step time t(N) for sparse trees of N nodes (the most accurate combinations)
+    and for the dense Cartesian tree, on the workload's weights and KV prefix.  E[a](N)
+    comes from the synthetic accuracy table drawn over the union of the trees' ranks; the
+    predicted rate is (1 + E[a]) / t(N) per sequence."""
+    import dataclasses
+    import numpy as np
+    from speculative_decoding_amd import budget
+    from synth.gen import accuracy_table
+    dense_s = SWEEP_DENSE.get(cfg.K)
+    s = tuple(max(a, b) for a, b in zip(cfg.s, dense_s)) if dense_s else tuple(cfg.s)
+    scfg = dataclasses.replace(cfg, s=s, tree_s=s)
+    acc = accuracy_table(scfg, seed)
+    dims = Dims.from_config(scfg)
+    n_cands = sum(int(np.prod(s[:d])) for d in range(1, len(s) + 1))
+    counts = [n for n in node_counts if 1 <= n <= min(n_cands + 1, M.MEDUSA_MAX_NODES)]
+
+    def timed(plan):
+        plan.upload(dev)
+        st = MedusaStep(dims, w, plan, dev)
+        st.heads(bootstrap_root=True)
+        for _ in range(warmup):
+            st.run(bootstrap_root=False, keep_u=False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.run(bootstrap_root=False, keep_u=False)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    pts = budget.curve(acc, s, counts, step_seconds=timed, dense_s=dense_s)
+    top = budget.best(pts)
+    sparse = {p.nodes: p for p in pts if p.kind == "sparse"}
+    dense = next((p for p in pts if p.kind == "dense"), None)
+    out = {"tree_s": list(s), "steps_per_point": steps,
+           "accuracy": "synthetic per-head rank accuracies 0.8*0.8^k*0.6*0.4^r*U(0.9,1.1), "
+                       "heads independent; E[a] is the closed form, not a measured rate",
+           "points": [p.as_dict() for p in pts],
+           "best": top.as_dict()}
+    if dense is not None and 64 in sparse:
+        out["sparse64_vs_dense"] = sparse[64].tokens_per_s / dense.tokens_per_s
+    return out
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -178,6 +227,10 @@ def main() -> int:
     ap.add_argument("--loop-rounds", type=int, default=32,
                     help="also time this many rounds of the decode loop (step + advance) on a "
                          "copy of the inputs whose KV cache has room for them (0: skip)")
+    ap.add_argument("--sweep-nodes", default=SWEEP_NODES,
+                    help="comma-separated sparse tree sizes for the node-budget sweep, timed "
+                         "after the main measurement (empty: skip)")
+    ap.add_argument("--sweep-steps", type=int, default=40)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run an elementwise kernel that reads and writes this many MiB once before "
                          "the timed region (known sizes to calibrate rocprofv3 byte counters)")
@@ -264,6 +317,12 @@ def main() -> int:
 
     res = step.results()
     loop = decode_loop_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, args.loop_rounds)
+    sweep = None
+    counts = [int(x) for x in args.sweep_nodes.split(",") if x.strip()]
+    if counts:
+        log(f"[bench] node-budget sweep over {counts}")
+        sweep = node_sweep(torch, M, MedusaStep, Dims, cfg, w, dev, args.seed, counts,
+                           args.sweep_steps, max(3, args.sweep_steps // 5))
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "cus": props.multi_processor_count,
               "arch": getattr(props, "gcnArchName", ""), "hbm_gib": round(props.total_memory / 2**30)}
@@ -272,14 +331,7 @@ def main() -> int:
     ab = algorithmic_bytes(cfg, n_nodes, prefix_total)
     sec = elapsed / args.steps
     steps_per_s = 1.0 / sec
-    expect_a = 0.0
-    parent, depth, rank, _ = plan.arrays()
-    for i in range(1, n_nodes):
-        p, j = 1.0, i
-        while j > 0:
-            p *= float(inp.acc[depth[j] - 1, rank[j]])
-            j = parent[j]
-        expect_a += p
+    expect_a = plan.expected_accept(inp.acc)
     mean_a = float(np.mean(a))
     roof = None
     if dom_n:
@@ -314,6 +366,7 @@ def main() -> int:
         "roofline": roof,
         "kernels": kernels,
         "decode_loop": loop,
+        "node_sweep": sweep,
         "device": device,
         "kernels_note": "per-kernel averages from a second pass of the same steps with every "
                         "launch event-timed (not the timed region)",

@@ -97,6 +97,16 @@ medusa_status medusa_tree_plan_from_accuracy(const double* acc, int acc_stride,
                                              const int32_t* tree_s, int depth, int n_nodes,
                                              medusa_tree_plan** out);
 
+/* Expected accepted length of a plan under per-head rank accuracies (same section: the
+ * sparse tree is the set of most accurate combinations, and a 64-node such tree is said to
+ * beat a 256-node dense one).  acc[(d-1)*acc_stride + r] is the probability that head d's
+ * rank-r candidate is the base model's next token at depth d (host doubles in [0, 1],
+ * heads independent, acc_rows >= the plan's max_depth, acc_stride >= every rank used + 1).
+ * Siblings exclude one another, so E[a] = sum over non-root nodes of the product of acc
+ * along the node's path; *out receives it (0 for a root-only plan).  Host only. */
+medusa_status medusa_tree_plan_expected_accept(const medusa_tree_plan* plan, const double* acc,
+                                               int acc_stride, int acc_rows, double* out);
+
 /* Shape of a plan: node count, deepest depth, 64-bit words per mask row. */
 medusa_status medusa_tree_plan_info(const medusa_tree_plan* plan, int* n_nodes, int* max_depth,
                                     int* mask_words);

@@ -27,6 +27,7 @@ _SIGS = {
     "medusa_tree_plan_info": (c_int, [c_void_p, ctypes.POINTER(c_int), ctypes.POINTER(c_int),
                                       ctypes.POINTER(c_int)]),
     "medusa_tree_plan_arrays": (c_int, [c_void_p, P_i32, P_i32, P_i32, P_u64]),
+    "medusa_tree_plan_expected_accept": (c_int, [c_void_p, P_f64, c_int, c_int, P_f64]),
     "medusa_tree_plan_device_bytes": (c_size_t, [c_void_p]),
     "medusa_tree_plan_upload": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p]),
     "medusa_tree_plan_destroy": (None, [c_void_p]),

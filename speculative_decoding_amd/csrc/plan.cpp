@@ -178,6 +178,23 @@ medusa_status medusa_tree_plan_from_accuracy(const double* acc, int acc_stride,
     return finish(std::move(keep), out);
 }
 
+medusa_status medusa_tree_plan_expected_accept(const medusa_tree_plan* plan, const double* acc,
+                                               int acc_stride, int acc_rows, double* out) {
+    if (!plan || !acc || !out) return MEDUSA_ERR_NULL;
+    if (acc_rows < plan->max_depth || acc_stride < 1) return MEDUSA_ERR_SHAPE;
+    // nodes are breadth first, so a parent's path probability is known before its children's
+    std::vector<double> path(plan->n_nodes, 1.0);
+    double sum = 0.0;
+    for (int i = 1; i < plan->n_nodes; ++i) {
+        const int d = plan->depth[i], r = plan->rank[i];
+        if (r >= acc_stride) return MEDUSA_ERR_SHAPE;
+        path[i] = path[plan->parent[i]] * acc[(size_t)(d - 1) * acc_stride + r];
+        sum += path[i];
+    }
+    *out = sum;
+    return MEDUSA_OK;
+}
+
 medusa_status medusa_tree_plan_info(const medusa_tree_plan* plan, int* n_nodes, int* max_depth,
                                     int* mask_words) {
     if (!plan) return MEDUSA_ERR_NULL;

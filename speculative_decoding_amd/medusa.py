@@ -14,6 +14,7 @@ import numpy as np
 from ._lib import lib
 
 MEDUSA_F32, MEDUSA_BF16 = 0, 1
+MEDUSA_MAX_TOPK, MEDUSA_MAX_HEADS, MEDUSA_MAX_NODES = 64, 8, 1024   # limits of include/medusa.h
 DTYPES = {"f32": MEDUSA_F32, "bf16": MEDUSA_BF16}
 
 
@@ -116,6 +117,15 @@ class TreePlan:
             P(mask, ctypes.c_uint64)))
         return parent, depth, rank, mask.reshape(n, w)
 
+    def expected_accept(self, acc: np.ndarray) -> float:
+        """Expected accepted length under per-head rank accuracies acc[depth-1][rank]."""
+        acc = np.ascontiguousarray(acc, dtype=np.float64)
+        out = ctypes.c_double()
+        _check("medusa_tree_plan_expected_accept", lib().medusa_tree_plan_expected_accept(
+            self._h, acc.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), acc.shape[1],
+            acc.shape[0], ctypes.byref(out)))
+        return out.value
+
     def device_bytes(self) -> int:
         return int(lib().medusa_tree_plan_device_bytes(self._h))
 
@@ -164,6 +174,10 @@ def medusa_tree_plan_from_accuracy(acc: np.ndarray, tree_s: Sequence[int], n_nod
         acc.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), acc.shape[1], _i32_host(tree_s),
         len(tree_s), int(n_nodes), ctypes.byref(out)))
     return TreePlan(out)
+
+
+def medusa_tree_plan_expected_accept(plan: TreePlan, acc: np.ndarray) -> float:
+    return plan.expected_accept(acc)
 
 
 # ------------------------------------------------------------------ the four calls

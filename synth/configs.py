@@ -129,6 +129,18 @@ CONFIGS = {
         tree_s=(4, 4, 4), n_nodes=85, Hq=4, Hkv=2, d=64, lens=(100, 257), Lcap=260,
         sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
         sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
+    # node budgets at the small shape: the root alone (no candidates, one verified row per
+    # sequence) and a wide 341-node tree (several 64-row blocks with a ragged last one)
+    "small_n1": Config(
+        name="small_n1", B=1, H=512, V=5003, K=4, s=(10, 5, 4, 3), tree="sparse",
+        tree_s=(10, 5, 4, 3), n_nodes=1, Hq=8, Hkv=2, d=128, L=300, Lcap=320,
+        sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
+        sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
+    "small_n341": Config(
+        name="small_n341", B=1, H=512, V=5003, K=4, s=(10, 5, 4, 3), tree="sparse",
+        tree_s=(10, 5, 4, 3), n_nodes=341, Hq=8, Hkv=2, d=128, L=300, Lcap=320,
+        sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
+        sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
     # decode-loop cases: room in the KV cache for several rounds of accepted branches
     "tiny_loop": Config(
         name="tiny_loop", B=1, H=256, V=1000, K=3, s=(2, 3, 3), tree="full", tree_s=(2, 3),
