@@ -33,6 +33,11 @@ Steps and the passages they follow:
   argmax is emitted after it (the blog page "Medusa no contexto de LLMs",
   section "o que significa medusa na prática de deploy": on rejection, fall
   back to the conventionally generated token).
+* ``softmax_entropy``, ``typical_accept`` — typical acceptance for sampling
+  (glossary, section "Attention arborescente et acceptation": keep every
+  candidate whose probability under the base model exceeds a threshold tied
+  to the entropy of that distribution).  The page gives no formula; the
+  readings are in ``typical_accept``'s docstring.
 * ``advance``, ``decode_loop`` — the next round: the longest accepted branch is
   kept and its last hidden state feeds the heads (glossary, section "Attention
   arborescente et acceptation").  The branch's rows join the KV cache, the
@@ -56,7 +61,7 @@ __all__ = [
     "as_f64", "round_act", "silu", "matvec_rows", "heads_forward", "lm_head_logits", "topk",
     "argmax_lowest", "build_tree", "proxy_qkv", "tree_attention", "proxy_out", "verify",
     "accept", "greedy_decode", "StepResult", "step", "causal_attention_last", "store_act",
-    "advance", "decode_loop",
+    "advance", "decode_loop", "softmax_entropy", "typical_accept",
 ]
 
 _CHUNK_ROWS = 8192
@@ -388,6 +393,69 @@ def step(inp, plan: TreePlan, root: Optional[np.ndarray] = None) -> StepResult:
                       topk_vals=vals, u=u, tokens=tokens, pos=pos, x=x, q=q, k=k, v=v, o=o,
                       node_hidden=nh, logits=logits, node_argmax=am, accept_len=alen,
                       accept_nodes=anodes, accept_tokens=atoks)
+
+
+# ----------------------------------------------------------------- typical acceptance
+
+def softmax_entropy(logits: np.ndarray, temperature: float):
+    """The base model's distribution over the vocabulary at temperature T,
+    p = softmax(logits / T) along the last axis, and its entropy in nats,
+    H = -sum_j p_j ln p_j (0 ln 0 = 0).  Returns (p, H)."""
+    z = np.asarray(logits, dtype=np.float64) / float(temperature)
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    p = e / e.sum(axis=-1, keepdims=True)
+    safe = np.where(p > 0.0, p, 1.0)
+    H = -(p * np.log(safe)).sum(axis=-1)
+    return p, H
+
+
+def typical_accept(plan: TreePlan, tokens: np.ndarray, logits: np.ndarray,
+                   node_argmax: np.ndarray, temperature: float, epsilon: float, delta: float):
+    """Typical acceptance of the tree's candidates (glossary, section "Attention
+    arborescente et acceptation": for sampling, every candidate whose base-model
+    probability exceeds an entropy-linked threshold is kept; more tokens pass
+    than under greedy matching, and exact agreement with the base model's
+    distribution is given up).
+
+    Readings, since the page gives no formula:
+    * node i's base-model distribution is p_i = softmax(logits_i / T) over the
+      vocabulary, H_i its entropy in nats (``softmax_entropy``);
+    * the threshold falls as the distribution flattens, capped:
+      tau_i = min(epsilon, delta * exp(-H_i));
+    * a child c of node i is accepted when i is accepted and
+      p_i(token_c) > tau_i (strict); several siblings may pass;
+    * the kept branch ends at the deepest accepted node, the lowest index among
+      equals (breadth-first order puts higher-ranked candidates first); it
+      emits its candidates, then that node's most probable token (its argmax),
+      as greedy acceptance does.
+
+    Returns accept_len [B], accept_nodes and accept_tokens [B, D+1] (as
+    ``accept``), node_prob [B, N] (p of each node's token under its parent's
+    distribution; 1 for the root) and node_tau [B, N] (tau_i)."""
+    B, N = tokens.shape
+    D = plan.max_depth
+    p, H = softmax_entropy(logits, temperature)
+    tau = np.minimum(float(epsilon), float(delta) * np.exp(-H))
+    prob = np.ones((B, N), dtype=np.float64)
+    alen = np.zeros(B, dtype=np.int64)
+    anodes = np.full((B, D + 1), -1, dtype=np.int64)
+    atoks = np.full((B, D + 1), -1, dtype=np.int64)
+    for b in range(B):
+        acc = np.zeros(N, dtype=bool)
+        acc[0] = True
+        for i in range(1, N):     # breadth-first order: parents come first
+            par = int(plan.parent[i])
+            prob[b, i] = p[b, par, int(tokens[b, i])]
+            acc[i] = acc[par] and prob[b, i] > tau[b, par]
+        deepest = max((i for i in range(N) if acc[i]), key=lambda i: (plan.depth[i], -i))
+        path = plan.path_nodes(deepest)
+        a = len(path) - 1
+        alen[b] = a
+        anodes[b, : a + 1] = path
+        atoks[b, :a] = [tokens[b, i] for i in path[1:]]
+        atoks[b, a] = node_argmax[b, deepest]
+    return alen, anodes, atoks, prob, tau
 
 
 # ----------------------------------------------------------------- the next round

@@ -382,3 +382,126 @@ def test_advance_rejects_a_full_cache():
     res = oracle.step(inp, plan)
     with pytest.raises(ValueError):
         oracle.advance(inp, plan, res)
+
+
+# ------------------------------------------------------------------ typical acceptance
+
+NEG = -1e30     # a logit whose probability underflows to exactly 0 at any temperature used
+
+
+@pytest.mark.parametrize("T", [0.05, 0.7, 1.0, 3.0])
+def test_softmax_entropy_against_scipy(T):
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    g = np.random.default_rng(11)
+    lg = g.normal(size=(3, 5, 257)) * 2.0
+    p, H = oracle.softmax_entropy(lg, T)
+    np.testing.assert_allclose(p, softmax(lg / T, axis=-1), rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(H, entropy(p, axis=-1), rtol=1e-10, atol=1e-13)
+
+
+def test_softmax_entropy_closed_forms():
+    # uniform over m of V tokens: p = 1/m, H = ln m, at any temperature
+    for m, T in ((1, 1.0), (4, 0.3), (7, 2.0)):
+        lg = np.full(50, NEG)
+        lg[[3, 9, 11, 20, 21, 33, 40][:m]] = 1.25
+        p, H = oracle.softmax_entropy(lg, T)
+        assert abs(H - math.log(m)) < 1e-12
+        assert np.allclose(p[lg > NEG], 1.0 / m, rtol=1e-13, atol=0) and p[lg == NEG].max() == 0.0
+    # two tokens a, b: p_a = 1 / (1 + e^{-(a-b)/T}), H = binary entropy
+    lg = np.full(10, NEG)
+    lg[2], lg[5] = 0.9, -0.4
+    p, H = oracle.softmax_entropy(lg, 0.5)
+    pa = 1.0 / (1.0 + math.exp(-(0.9 + 0.4) / 0.5))
+    assert abs(p[2] - pa) < 1e-15 and abs(p[5] - (1.0 - pa)) < 1e-15
+    assert abs(H - (-pa * math.log(pa) - (1 - pa) * math.log(1 - pa))) < 1e-14
+
+
+def _typical_case():
+    """The 2x3 tree of the page's example with hand-set distributions (vocabulary 100).
+    Nodes: 0 root; 1 = (0,) token 10, 2 = (1,) token 11; 3..5 = (0, r) tokens 20, 21, 22;
+    6..8 = (1, r) tokens 20, 21, 22."""
+    plan = oracle.plan_full((2, 3))
+    tokens = np.array([[5, 10, 11, 20, 21, 22, 20, 21, 22]])
+    lg = np.full((1, 9, 100), NEG)
+    lg[0, 0, [10, 11]] = 0.0                    # root: 1/2 each, H = ln 2
+    lg[0, 1, [20, 21, 22, 23]] = 1.0            # node 1: 1/4 each, H = ln 4
+    lg[0, 2, 20] = math.log(9.0)                # node 2: token 20 at 9/10, token 50 at 1/10
+    lg[0, 2, 50] = 0.0
+    lg[0, 3, 77] = 0.0                          # node 3: all mass on 77
+    for i in range(4, 9):
+        lg[0, i, 60 + i] = 0.0
+    am = np.array([[int(np.argmax(lg[0, i])) for i in range(9)]])
+    return plan, tokens, lg, am
+
+
+def test_typical_accept_hand_case():
+    plan, tokens, lg, am = _typical_case()
+    # eps 0.3, delta 0.4: tau_root = min(0.3, 0.4/2) = 0.2 < 1/2 -> nodes 1 and 2 pass;
+    # tau_1 = min(0.3, 0.4/4) = 0.1 < 1/4 -> nodes 3, 4, 5 pass; under node 2 only token 20
+    # (9/10) passes (node 6).  Deepest: depth 2, lowest index: node 3.
+    a, nodes, toks, prob, tau = oracle.typical_accept(plan, tokens, lg, am, 1.0, 0.3, 0.4)
+    assert a.tolist() == [2] and nodes[0].tolist() == [0, 1, 3] and toks[0].tolist() == [10, 20, 77]
+    np.testing.assert_allclose(prob[0], [1, 0.5, 0.5, 0.25, 0.25, 0.25, 0.9, 0, 0], rtol=1e-14,
+                               atol=1e-300)
+    h2 = -(0.9 * math.log(0.9) + 0.1 * math.log(0.1))
+    np.testing.assert_allclose(tau[0, :3], [0.2, 0.1, min(0.3, 0.4 * math.exp(-h2))], rtol=1e-14)
+    # a threshold above 1/2 at the root: nothing passes, the root's argmax (lowest id of the
+    # tie: 10) is emitted
+    a, nodes, toks, _, tau = oracle.typical_accept(plan, tokens, lg, am, 1.0, 0.6, 1.5)
+    assert abs(tau[0, 0] - 0.6) < 1e-15
+    assert a.tolist() == [0] and nodes[0].tolist() == [0, -1, -1] and toks[0].tolist() == [10, -1, -1]
+    # equality does not pass: tau_1 = min(0.25, 10/4) = 1/4 = p of node 1's children, so
+    # the branch continues only under node 2 (token 20 at 9/10 > 1/4: node 6)
+    a, nodes, toks, prob, tau = oracle.typical_accept(plan, tokens, lg, am, 1.0, 0.25, 10.0)
+    assert tau[0, 1] == 0.25 and prob[0, 3] == 0.25
+    assert a.tolist() == [2] and nodes[0].tolist() == [0, 2, 6] and toks[0].tolist() == [11, 20, 66]
+
+
+@pytest.mark.parametrize("cfg,seed", [("tiny", 0), ("tiny", 3), ("small", 1), ("small_batched", 0)])
+def test_typical_at_low_temperature_is_greedy(cfg, seed):
+    """As T -> 0 the distribution concentrates on the argmax (planted margins >= 1e-2 give
+    p(argmax) = 1 and p(other) = 0 in fp64 at T = 1e-6) and its entropy on 0, so a
+    candidate passes exactly when it is the argmax: greedy acceptance."""
+    from tests import planting
+    inp = planting.planted_inputs(cfg, seed)
+    plan = planting.plan_for(inp.cfg, inp.acc)
+    res = oracle.step(inp, plan)
+    a, nodes, toks, prob, _ = oracle.typical_accept(plan, res.tokens, res.logits, res.node_argmax,
+                                                    1e-6, 0.3, 0.09)
+    assert np.array_equal(a, res.accept_len)
+    assert np.array_equal(nodes, res.accept_nodes) and np.array_equal(toks, res.accept_tokens)
+    assert set(np.unique(prob).tolist()) <= {0.0, 1.0}
+
+
+def test_typical_threshold_extremes():
+    from tests import planting
+    inp = planting.planted_inputs("small_batched", 0)
+    plan = planting.plan_for(inp.cfg, inp.acc)
+    res = oracle.step(inp, plan)
+    # delta = 0: tau = 0 and every finite logit has p > 0, so every node passes; the kept
+    # branch ends at the first deepest node
+    a, nodes, toks, prob, tau = oracle.typical_accept(plan, res.tokens, res.logits,
+                                                      res.node_argmax, 1.0, 0.5, 0.0)
+    first_deep = min(i for i in range(plan.n_nodes) if plan.depth[i] == plan.max_depth)
+    assert (prob > 0).all() and (tau == 0).all()
+    for b in range(inp.cfg.B):
+        assert a[b] == plan.max_depth and nodes[b].tolist() == plan.path_nodes(first_deep)
+        assert toks[b, -1] == res.node_argmax[b, first_deep]
+    # tau above 1: nothing passes; only the root's argmax is emitted
+    a, nodes, toks, _, _ = oracle.typical_accept(plan, res.tokens, res.logits, res.node_argmax,
+                                                 1.0, 2.0, 1e9)
+    assert (a == 0).all() and (toks[:, 0] == res.node_argmax[:, 0]).all()
+
+
+def test_typical_higher_threshold_never_accepts_more():
+    from tests import planting
+    inp = planting.planted_inputs("small", 0)
+    plan = planting.plan_for(inp.cfg, inp.acc)
+    res = oracle.step(inp, plan)
+    prev = None
+    for eps in (1e-9, 1e-6, 1e-5, 1e-4, 1e-3, 1e-2, 0.1, 1.0):
+        a = oracle.typical_accept(plan, res.tokens, res.logits, res.node_argmax, 1.0, eps, 1.0)[0]
+        if prev is not None:
+            assert (a <= prev).all()
+        prev = a
