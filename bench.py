@@ -153,6 +153,40 @@ def node_sweep(torch, M, MedusaStep, Dims, cfg, w, dev, seed: int, node_counts, 
     return out
 
 
+TYPICAL = (1.0, 0.09, 0.3)          # temperature, epsilon, delta: values chosen here
+
+
+def typical_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, steps: int, warmup: int):
+    """Whole steps with typical acceptance (medusa_verify_accept_typical) in place of greedy
+    acceptance, on the same inputs and plan, then a pass with every launch event-timed for
+    the two verification kernels."""
+    st = MedusaStep(Dims.from_config(cfg), w, plan, dev, typical=TYPICAL)
+    st.heads(bootstrap_root=True)
+    for _ in range(warmup):
+        st.run(bootstrap_root=False, keep_u=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.run(bootstrap_root=False, keep_u=False)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    M.medusa_profile_reset()
+    M.medusa_profile_only(None)
+    M.medusa_profile_enable(True)
+    for _ in range(steps):
+        st.run(bootstrap_root=False, keep_u=False)
+    torch.cuda.synchronize()
+    M.medusa_profile_enable(False)
+    out = {"temperature": TYPICAL[0], "epsilon": TYPICAL[1], "delta": TYPICAL[2],
+           "steps": steps, "ms_per_step": 1e3 * sec, "steps_per_s": 1.0 / sec,
+           "accept_len": [int(x) for x in st.accept_len.cpu()]}
+    for name in ("verify_lmhead", "verify_accept"):
+        ms, n = M.medusa_profile_query(name)
+        if n:
+            out[name + "_us"] = 1e3 * ms / n
+    return out
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -231,6 +265,8 @@ def main() -> int:
                     help="comma-separated sparse tree sizes for the node-budget sweep, timed "
                          "after the main measurement (empty: skip)")
     ap.add_argument("--sweep-steps", type=int, default=40)
+    ap.add_argument("--typical-steps", type=int, default=100,
+                    help="whole steps timed with typical acceptance (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run an elementwise kernel that reads and writes this many MiB once before "
                          "the timed region (known sizes to calibrate rocprofv3 byte counters)")
@@ -317,6 +353,11 @@ def main() -> int:
 
     res = step.results()
     loop = decode_loop_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, args.loop_rounds)
+    typical = None
+    if args.typical_steps > 0:
+        log("[bench] typical acceptance")
+        typical = typical_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, args.typical_steps,
+                               max(3, args.typical_steps // 10))
     sweep = None
     counts = [int(x) for x in args.sweep_nodes.split(",") if x.strip()]
     if counts:
@@ -367,6 +408,7 @@ def main() -> int:
         "kernels": kernels,
         "decode_loop": loop,
         "node_sweep": sweep,
+        "typical": typical,
         "device": device,
         "kernels_note": "per-kernel averages from a second pass of the same steps with every "
                         "launch event-timed (not the timed region)",

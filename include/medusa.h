@@ -199,6 +199,32 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
                                    size_t ws_bytes, void* stream);
 size_t medusa_verify_workspace(const medusa_tree_plan* plan, medusa_dtype dt, int B, int H, int V);
 
+/* Typical acceptance, for sampling (same section: every candidate whose probability under
+ * the base model exceeds a threshold tied to the entropy of that distribution is kept; more
+ * tokens pass, exact agreement with the base model's distribution is given up).  The page
+ * gives no formula; this library reads it as
+ *     p_i = softmax(logits_i / temperature) over the vocabulary,  H_i = -sum p_i ln p_i,
+ *     tau_i = min(epsilon, delta * exp(-H_i)),
+ *     node c >= 1 accepted iff its parent i is accepted and p_i(node_tokens[c]) > tau_i.
+ * Several siblings may pass; the kept branch ends at the deepest accepted node, the lowest
+ * index among equals, and emits its candidates and then that node's argmax a_{i*}, as in
+ * medusa_verify_accept (same output layouts).  Optional outputs: node_argmax [B,N] int32,
+ * node_prob [B,N] fp32 (p of each node's token under its parent's distribution; 1 for the
+ * root), node_tau [B,N] fp32 (tau_i), logits [B,N,V] fp32.  Arithmetic is fp32; the
+ * softmax sums are merged over vocabulary tiles in a fixed order.
+ * 1e-6 <= temperature <= 1e6; epsilon, delta finite and >= 0 (else MEDUSA_ERR_SHAPE).
+ * ws/ws_bytes: at least medusa_verify_typical_workspace() bytes. */
+medusa_status medusa_verify_accept_typical(const medusa_tree_plan* plan, medusa_dtype dt, int B,
+                                           int H, int V, const void* node_hidden, const void* w_lm,
+                                           const int32_t* node_tokens, float temperature,
+                                           float epsilon, float delta, int32_t* node_argmax,
+                                           float* node_prob, float* node_tau, int32_t* accept_len,
+                                           int32_t* accept_nodes, int32_t* accept_tokens,
+                                           float* logits, void* ws, size_t ws_bytes,
+                                           void* stream);
+size_t medusa_verify_typical_workspace(const medusa_tree_plan* plan, medusa_dtype dt, int B,
+                                       int H, int V);
+
 /* ------------------------------------------------------------------ 5. next round
  * Commit each sequence's accepted branch and set up the next step (glossary, "Attention
  * arborescente et acceptation": the longest accepted branch is kept and its last hidden

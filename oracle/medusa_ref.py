@@ -61,7 +61,7 @@ __all__ = [
     "as_f64", "round_act", "silu", "matvec_rows", "heads_forward", "lm_head_logits", "topk",
     "argmax_lowest", "build_tree", "proxy_qkv", "tree_attention", "proxy_out", "verify",
     "accept", "greedy_decode", "StepResult", "step", "causal_attention_last", "store_act",
-    "advance", "decode_loop", "softmax_entropy", "typical_accept",
+    "advance", "decode_loop", "softmax_entropy", "typical_accept", "typical_branch",
 ]
 
 _CHUNK_ROWS = 8192
@@ -434,10 +434,24 @@ def typical_accept(plan: TreePlan, tokens: np.ndarray, logits: np.ndarray,
     ``accept``), node_prob [B, N] (p of each node's token under its parent's
     distribution; 1 for the root) and node_tau [B, N] (tau_i)."""
     B, N = tokens.shape
-    D = plan.max_depth
     p, H = softmax_entropy(logits, temperature)
     tau = np.minimum(float(epsilon), float(delta) * np.exp(-H))
     prob = np.ones((B, N), dtype=np.float64)
+    for b in range(B):
+        for i in range(1, N):
+            prob[b, i] = p[b, int(plan.parent[i]), int(tokens[b, i])]
+    alen, anodes, atoks = typical_branch(plan, tokens, node_argmax, prob, tau)
+    return alen, anodes, atoks, prob, tau
+
+
+def typical_branch(plan: TreePlan, tokens: np.ndarray, node_argmax: np.ndarray,
+                   prob: np.ndarray, tau: np.ndarray):
+    """The walk of ``typical_accept`` given each node's probability under its parent's
+    distribution (prob [B, N]) and each node's threshold (tau [B, N]): node i >= 1 is
+    accepted when its parent is and prob[i] > tau[parent]; the kept branch ends at the
+    deepest accepted node, the lowest index among equals."""
+    B, N = tokens.shape
+    D = plan.max_depth
     alen = np.zeros(B, dtype=np.int64)
     anodes = np.full((B, D + 1), -1, dtype=np.int64)
     atoks = np.full((B, D + 1), -1, dtype=np.int64)
@@ -446,7 +460,6 @@ def typical_accept(plan: TreePlan, tokens: np.ndarray, logits: np.ndarray,
         acc[0] = True
         for i in range(1, N):     # breadth-first order: parents come first
             par = int(plan.parent[i])
-            prob[b, i] = p[b, par, int(tokens[b, i])]
             acc[i] = acc[par] and prob[b, i] > tau[b, par]
         deepest = max((i for i in range(N) if acc[i]), key=lambda i: (plan.depth[i], -i))
         path = plan.path_nodes(deepest)
@@ -455,7 +468,7 @@ def typical_accept(plan: TreePlan, tokens: np.ndarray, logits: np.ndarray,
         anodes[b, : a + 1] = path
         atoks[b, :a] = [tokens[b, i] for i in path[1:]]
         atoks[b, a] = node_argmax[b, deepest]
-    return alen, anodes, atoks, prob, tau
+    return alen, anodes, atoks
 
 
 # ----------------------------------------------------------------- the next round

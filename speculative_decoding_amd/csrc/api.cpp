@@ -57,16 +57,24 @@ HeadsLayout heads_layout(medusa_dtype dt, int B, int H, int V, int K, int s_max,
 }
 
 struct VerifyLayout {
-    size_t part_val = 0, part_idx = 0, total = 0;
+    size_t part_val = 0, part_idx = 0, part_z = 0, part_s = 0, cand_logit = 0, total = 0;
     int n_tiles = 0;
 };
 
-VerifyLayout verify_layout(medusa_dtype dt, int M, int V, int H) {
+// Greedy verification needs the per-tile argmax partials; typical acceptance adds the
+// per-tile softmax sums and one candidate logit per node (same tiles: EPI_TYPICAL shares
+// EPI_ARGMAX's kernels and tile sizes).
+VerifyLayout verify_layout(medusa_dtype dt, int M, int V, int H, bool typical = false) {
     VerifyLayout L;
     Carver c;
     L.n_tiles = n_tiles_for(dt, M, EPI_ARGMAX, V, H);
     L.part_val = c.take((size_t)M * L.n_tiles * sizeof(float));
     L.part_idx = c.take((size_t)M * L.n_tiles * sizeof(int32_t));
+    if (typical) {
+        L.part_z = c.take((size_t)M * L.n_tiles * sizeof(float));
+        L.part_s = c.take((size_t)M * L.n_tiles * sizeof(float));
+        L.cand_logit = c.take((size_t)M * sizeof(float));
+    }
     L.total = c.off;
     return L;
 }
@@ -346,6 +354,90 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
     prof_begin("verify_accept", strm);
     e = accept_launch(medusa_internal_device_plan(plan), B, L.n_tiles, pv, pi, node_tokens,
                       node_argmax, accept_len, accept_nodes, accept_tokens, strm);
+    prof_end(strm);
+    if (e != hipSuccess) return medusa_internal_hip_error(e);
+    return MEDUSA_OK;
+}
+
+size_t medusa_verify_typical_workspace(const medusa_tree_plan* plan, medusa_dtype dt, int B,
+                                       int H, int V) {
+    if (!plan || !dtype_ok(dt) || B < 1 || H < 1 || V < 1) return 0;
+    return verify_layout(dt, B * plan->n_nodes, V, H, true).total;
+}
+
+medusa_status medusa_verify_accept_typical(const medusa_tree_plan* plan, medusa_dtype dt, int B,
+                                           int H, int V, const void* node_hidden, const void* w_lm,
+                                           const int32_t* node_tokens, float temperature,
+                                           float epsilon, float delta, int32_t* node_argmax,
+                                           float* node_prob, float* node_tau, int32_t* accept_len,
+                                           int32_t* accept_nodes, int32_t* accept_tokens,
+                                           float* logits, void* ws, size_t ws_bytes,
+                                           void* stream) {
+    if (!plan || !node_hidden || !w_lm || !node_tokens || !accept_len || !accept_nodes ||
+        !accept_tokens)
+        return MEDUSA_ERR_NULL;
+    if (!dtype_ok(dt)) return MEDUSA_ERR_UNSUPPORTED;
+    if (B < 1 || B > 4096 || H < 32 || H > 16384 || H % 32 != 0 || V < 1) return MEDUSA_ERR_SHAPE;
+    if (!(temperature >= 1e-6f && temperature <= 1e6f) || !(epsilon >= 0.f) ||
+        !(delta >= 0.f) || !std::isfinite(epsilon) || !std::isfinite(delta))
+        return MEDUSA_ERR_SHAPE;
+    if (!aligned16(node_hidden) || !aligned16(w_lm)) return MEDUSA_ERR_SHAPE;
+    const int M = B * plan->n_nodes;
+    const VerifyLayout L = verify_layout(dt, M, V, H, true);
+    if (!ws || ws_bytes < L.total) return MEDUSA_ERR_WORKSPACE;
+    if (!plan->dev) return MEDUSA_ERR_PLAN_NOT_ON_DEVICE;
+    medusa_status st = medusa_internal_device_check();
+    if (st != MEDUSA_OK) return st;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    unsigned char* wsb = static_cast<unsigned char*>(ws);
+    const DevicePlan dp = medusa_internal_device_plan(plan);
+
+    GemmBatch g{};
+    g.n_problems = 1;
+    g.M = M;
+    g.K = H;
+    GemmProblem& p = g.p[0];
+    p.W = w_lm;
+    p.X = node_hidden;
+    p.x_stride = H;
+    p.N = V;
+    p.tile_begin = 0;
+    p.n_tiles = L.n_tiles;
+    p.s = 1;
+    p.part_val = reinterpret_cast<float*>(wsb + L.part_val);
+    p.part_idx = reinterpret_cast<int32_t*>(wsb + L.part_idx);
+    p.logits = logits;
+    p.logits_ld = V;
+    g.total_tiles = L.n_tiles;
+    g.typ.inv_t = 1.0f / temperature;
+    g.typ.part_z = reinterpret_cast<float*>(wsb + L.part_z);
+    g.typ.part_s = reinterpret_cast<float*>(wsb + L.part_s);
+    g.typ.parent = dp.parent;
+    g.typ.node_tokens = node_tokens;
+    g.typ.n_nodes = plan->n_nodes;
+    g.typ.cand_logit = reinterpret_cast<float*>(wsb + L.cand_logit);
+    hipError_t e = timed_gemm("verify_lmhead", dt, EPI_TYPICAL, g, strm);
+    if (e != hipSuccess) return medusa_internal_hip_error(e);
+
+    TypicalAccept ta{};
+    ta.n_tiles = L.n_tiles;
+    ta.part_val = p.part_val;
+    ta.part_idx = p.part_idx;
+    ta.part_z = g.typ.part_z;
+    ta.part_s = g.typ.part_s;
+    ta.cand_logit = g.typ.cand_logit;
+    ta.node_tokens = node_tokens;
+    ta.inv_t = g.typ.inv_t;
+    ta.epsilon = epsilon;
+    ta.delta = delta;
+    ta.node_argmax = node_argmax;
+    ta.node_prob = node_prob;
+    ta.node_tau = node_tau;
+    ta.accept_len = accept_len;
+    ta.accept_nodes = accept_nodes;
+    ta.accept_tokens = accept_tokens;
+    prof_begin("verify_accept", strm);
+    e = typical_accept_launch(dp, B, ta, strm);
     prof_end(strm);
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     return MEDUSA_OK;

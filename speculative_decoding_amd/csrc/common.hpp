@@ -134,6 +134,15 @@ __device__ __forceinline__ void row_best(float& v, int& i) {
     best_step<kDppMirror>(v, i);
 }
 
+// Sum over each row of 16 lanes in a fixed order; every lane of the row gets it.
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    return v;
+}
+
 // Best (value, id) over the whole wave; every lane gets it.
 __device__ __forceinline__ void wave_best(float& v, int& i) {
     row_best(v, i);

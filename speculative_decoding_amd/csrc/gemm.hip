@@ -34,6 +34,7 @@ constexpr int kSplitUnroll = 4;       // k-steps per load group in the split-con
 template <typename T, int EPI> struct StreamCfg { static constexpr int RT = 2, UN = 4; };
 template <> struct StreamCfg<bf16_t, EPI_TOPS> { static constexpr int RT = 2, UN = 8; };
 template <> struct StreamCfg<bf16_t, EPI_ARGMAX> { static constexpr int RT = 2, UN = 2; };
+template <typename T> struct StreamCfg<T, EPI_TYPICAL> : StreamCfg<T, EPI_ARGMAX> {};
 
 // acc[rt][mt][r] = Y[m0 + mt*16 + 4*lg + r][n_wave + rt*16 + ln]:
 // out[m][n] = rnd(silu?(Y + bias[n]) + residual[m][n]).
@@ -202,6 +203,100 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_store_kernel(const GemmB
     store_epilogue<T, MT, RT>(P, bt, acc, m0, n_wave, ln, lg);
 }
 
+// EPI_TYPICAL after the argmax: the tile's softmax sums of every row and the logits of the
+// tree candidates that fall in this wave's columns.  On entry red_v[0][row] holds the
+// tile's maximum of each row (written by the argmax merge); red_v / red_i are then reused
+// for the per-wave sums.  With x = (logit - tile max) / T: z = sum exp(x), s = sum exp(x) x.
+template <int MT, int RT, int NWV>
+__device__ __forceinline__ void typical_tile(const GemmProblem& P, const GemmBatch& bt,
+                                             const floatx4 (&acc)[RT][MT], int m0, int Mb,
+                                             int tile, int n_wave, int wave, int lane,
+                                             float (&red_v)[NWV][MT * 16],
+                                             int (&red_i)[NWV][MT * 16]) {
+    const TypicalEpi& ty = bt.typ;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int N = P.N;
+    constexpr float kLog2e = 1.4426950408889634f;
+    __syncthreads();
+    float tmax[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = mt * 16 + 4 * lg + r;
+            tmax[mt][r] = row < Mb ? red_v[0][row] : 0.f;
+        }
+    __syncthreads();        // every lane has its maxima before the sums overwrite red_v
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float z = 0.f, sx = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int n = n_wave + rt * 16 + ln;
+                if (n < N) {
+                    const float x = (acc[rt][mt][r] - tmax[mt][r]) * ty.inv_t;
+                    const float e = __builtin_amdgcn_exp2f(x * kLog2e);
+                    z += e;
+                    sx += e * x;
+                }
+            }
+            z = row_sum16(z);
+            sx = row_sum16(sx);
+            if (ln == 0) {
+                red_v[wave][mt * 16 + 4 * lg + r] = z;
+                red_i[wave][mt * 16 + 4 * lg + r] = __float_as_int(sx);
+            }
+        }
+    __syncthreads();
+    for (int m = threadIdx.x; m < Mb; m += NWV * kWave) {
+        float z = red_v[0][m];
+        float sx = __int_as_float(red_i[0][m]);
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) {
+            z += red_v[w][m];
+            sx += __int_as_float(red_i[w][m]);
+        }
+        const long long o = (long long)(m0 + m) * P.n_tiles + tile;
+        ty.part_z[o] = z;
+        ty.part_s[o] = sx;
+    }
+    // Candidate logits: 64 candidates at a time, each lane loads one (parent row, token);
+    // the few that fall in this wave's rows and columns are written by the lane holding them.
+    const int NN = ty.n_nodes;
+    const int b_lo = m0 / NN;
+    const int b_hi = (m0 + Mb - 1) / NN;
+    for (int b = b_lo; b <= b_hi; ++b) {
+        for (int c0 = 1; c0 < NN; c0 += kWave) {
+            const int c = c0 + lane;
+            int pr = -1, tok = -1;
+            if (c < NN) {
+                pr = b * NN + ty.parent[c];
+                tok = ty.node_tokens[(long long)b * NN + c];
+            }
+            const bool hit = c < NN && pr >= m0 && pr < m0 + Mb && tok >= n_wave &&
+                             tok < n_wave + RT * 16;
+            unsigned long long mask = __ballot(hit);
+            while (mask) {
+                const int src = __builtin_ctzll(mask);
+                mask &= mask - 1;
+                const int hp = __builtin_amdgcn_readlane(pr, src);
+                const int ht = __builtin_amdgcn_readlane(tok, src);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n_wave + rt * 16 + ln == ht && m0 + mt * 16 + 4 * lg + r == hp)
+                                ty.cand_logit[(long long)b * NN + c0 + src] = acc[rt][mt][r];
+            }
+        }
+    }
+}
+
 // Shared epilogue of the MFMA kernels: optional fp32 logits, then the per-tile argmax or
 // top-s of every input row.  acc[rt][mt][r] = Y[m0 + mt*16 + 4*lg + r][n_wave + rt*16 + ln];
 // `smem` must hold Mb * NWG floats (top-s only) and may alias the kernel's X staging area.
@@ -229,7 +324,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBa
         }
     }
 
-    if (EPI == EPI_ARGMAX) {
+    if (EPI == EPI_ARGMAX || EPI == EPI_TYPICAL) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -259,7 +354,10 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBa
             const long long o = (long long)(m0 + m) * P.n_tiles + tile;
             P.part_val[o] = bv;
             P.part_idx[o] = bi;
+            if (EPI == EPI_TYPICAL) red_v[0][m] = bv;     // this thread alone reads column m
         }
+        if (EPI == EPI_TYPICAL)
+            typical_tile<MT, RT, NWV>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane, red_v, red_i);
         return;
     }
 
@@ -970,7 +1068,7 @@ size_t slab_argmax_lds(int nw, int rt) {
     return (size_t)64 * (kSlab + 8) * 2 + (size_t)nw * 16 * rt * (64 + 8) * 2 + (size_t)nw * 64 * 8;
 }
 
-template <int NW, int RT, int PF>
+template <int NW, int RT, int PF, int EPI>
 __global__ __launch_bounds__(NW * kWave) void gemm_slab_argmax_kernel(const GemmBatch bt) {
     constexpr int MT = 4;
     constexpr int CH = 64;
@@ -1113,8 +1211,8 @@ __global__ __launch_bounds__(NW * kWave) void gemm_slab_argmax_kernel(const Gemm
         }
     }
     __syncthreads();
-    tile_epilogue<MT, RT, NWG, EPI_ARGMAX, NW>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane,
-                                               nullptr, red_v, red_i);
+    tile_epilogue<MT, RT, NWG, EPI, NW>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane, nullptr,
+                                        red_v, red_i);
 }
 
 #ifndef MEDUSA_SLAB_NW
@@ -1138,7 +1236,8 @@ constexpr int kSlabPf = MEDUSA_SLAB_PF;
 // the row-streaming kernel; at 64 rows two row-streaming workgroups per CU hide latency
 // better (170 against 176 us).
 __host__ bool slab_argmax_eligible(medusa_dtype dt, int epi, int M, int K) {
-    return MEDUSA_SLAB && dt == MEDUSA_BF16 && epi == EPI_ARGMAX && M > 64 && K % kSlab == 0;
+    return MEDUSA_SLAB && dt == MEDUSA_BF16 && (epi == EPI_ARGMAX || epi == EPI_TYPICAL) &&
+           M > 64 && K % kSlab == 0;
 }
 
 // Sum the contraction slices of every (m, n) in slice order and apply the store epilogue:
@@ -1551,6 +1650,7 @@ hipError_t launch_epi(int epi, GemmBatch& bt, hipStream_t stream) {
     switch (epi) {
         case EPI_STORE: return launch_store<T>(bt, stream);
         case EPI_TOPS: return launch_mt<T, EPI_TOPS>(bt, stream);
+        case EPI_TYPICAL: return launch_mt<T, EPI_TYPICAL>(bt, stream);
         default: return launch_mt<T, EPI_ARGMAX>(bt, stream);
     }
 }
@@ -1564,7 +1664,8 @@ int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
     if (epi == EPI_PARTIAL) return kWavePartialRows;
     if (slab_argmax_eligible(dt, epi, M, K)) return kSlabNw * 16 * kSlabRt;
     if (rowstream_eligible(dt, epi, M, K))
-        return epi == EPI_ARGMAX ? kRsWavesArgmax * 16 * kRsRtwArgmax : kWaves * 16 * kRsRtw;
+        return epi == EPI_ARGMAX || epi == EPI_TYPICAL ? kRsWavesArgmax * 16 * kRsRtwArgmax
+                                                       : kWaves * 16 * kRsRtw;
     int rt;
     if (dt == MEDUSA_BF16)
         rt = epi == EPI_TOPS ? StreamCfg<bf16_t, EPI_TOPS>::RT : StreamCfg<bf16_t, EPI_ARGMAX>::RT;
@@ -1628,11 +1729,14 @@ hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
 hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
     if (epi == EPI_TOPS)
         return launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunk, kWaves>(bt, stream);
+    if (epi == EPI_TYPICAL)
+        return launch_rowstream_m<EPI_TYPICAL, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
     return launch_rowstream_m<EPI_ARGMAX, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
 }
 
+template <int EPI>
 hipError_t launch_slab_argmax(GemmBatch& bt, hipStream_t stream) {
-    auto kern = gemm_slab_argmax_kernel<kSlabNw, kSlabRt, kSlabPf>;
+    auto kern = gemm_slab_argmax_kernel<kSlabNw, kSlabRt, kSlabPf, EPI>;
     const size_t lds = slab_argmax_lds(kSlabNw, kSlabRt);
     static bool attr = false;
     if (!attr) {
@@ -1650,7 +1754,7 @@ hipError_t launch_slab_argmax(GemmBatch& bt, hipStream_t stream) {
 // top-s epilogue (top-s only past the GEMV's two rows).
 bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K) {
     if (dt != MEDUSA_BF16 || K % kRsChunk != 0) return false;
-    return epi == EPI_ARGMAX || (epi == EPI_TOPS && M > 2);
+    return epi == EPI_ARGMAX || epi == EPI_TYPICAL || (epi == EPI_TOPS && M > 2);
 }
 
 #ifndef MEDUSA_KSPLIT_WG
@@ -1767,7 +1871,9 @@ hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& bt, hipStream_t
 }
 
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& bt, hipStream_t stream) {
-    if (slab_argmax_eligible(dt, epi, bt.M, bt.K)) return launch_slab_argmax(bt, stream);
+    if (slab_argmax_eligible(dt, epi, bt.M, bt.K))
+        return epi == EPI_TYPICAL ? launch_slab_argmax<EPI_TYPICAL>(bt, stream)
+                                  : launch_slab_argmax<EPI_ARGMAX>(bt, stream);
     if (rowstream_eligible(dt, epi, bt.M, bt.K)) return launch_rowstream(epi, bt, stream);
     if (gemv_eligible(dt, epi, bt))
         return epi == EPI_TOPS ? launch_gemv_k<EPI_TOPS>(bt, stream) : launch_gemv_k<EPI_STORE>(bt, stream);

@@ -19,6 +19,22 @@ enum Epilogue : int {
     EPI_TOPS = 1,    // per row m: the tile's top-s (value desc, id asc) -> partials
     EPI_ARGMAX = 2,  // per row m: the tile's best (value, id) -> partials
     EPI_PARTIAL = 3, // fp32 partial sums of one contraction slice -> part_val[slice][m][n]
+    EPI_TYPICAL = 4, // EPI_ARGMAX plus the tile's softmax sums and the tree candidates' logits
+};
+
+// Extra outputs of the EPI_TYPICAL epilogue (lm_head over the tree nodes; row m = b*n_nodes+i).
+// With x = (logit - tile max) / T per vocabulary entry of the tile:
+//   part_z[m][tile] = sum exp(x),  part_s[m][tile] = sum exp(x) * x
+// and for every non-root node c of sequence b, the logit of c's token in its parent's row:
+//   cand_logit[b*n_nodes + c] = logit[b*n_nodes + parent[c]][node_tokens[b*n_nodes + c]].
+struct TypicalEpi {
+    float inv_t;                 // 1 / temperature
+    float* part_z;               // [M, n_tiles]
+    float* part_s;
+    const int32_t* parent;       // the plan's parents (device)
+    const int32_t* node_tokens;  // [B, n_nodes]
+    int n_nodes;
+    float* cand_logit;           // [B, n_nodes]; root entries untouched
 };
 
 struct GemmProblem {
@@ -55,6 +71,7 @@ struct GemmBatch {
     int x_rows_bound;
     int res_rows_bound;
     int ksplit;               // contraction slices (EPI_PARTIAL); 1 otherwise
+    TypicalEpi typ;           // EPI_TYPICAL only
 };
 
 // Rows of W per workgroup for a given configuration.
@@ -111,6 +128,27 @@ hipError_t accept_launch(const DevicePlan& plan, int B, int n_tiles, const float
                          const int32_t* part_idx, const int32_t* node_tokens,
                          int32_t* node_argmax, int32_t* accept_len, int32_t* accept_nodes,
                          int32_t* accept_tokens, hipStream_t stream);
+// Typical acceptance from the EPI_TYPICAL partials: per node the argmax, the softmax
+// normaliser and entropy (merged over the tiles), the threshold min(epsilon, delta*exp(-H))
+// and each candidate's probability under its parent's distribution; then the branch walk.
+struct TypicalAccept {
+    int n_tiles;
+    const float* part_val;
+    const int32_t* part_idx;
+    const float* part_z;
+    const float* part_s;
+    const float* cand_logit;
+    const int32_t* node_tokens;
+    float inv_t, epsilon, delta;
+    int32_t* node_argmax;        // may be null
+    float* node_prob;            // may be null
+    float* node_tau;             // may be null
+    int32_t* accept_len;
+    int32_t* accept_nodes;
+    int32_t* accept_tokens;
+};
+hipError_t typical_accept_launch(const DevicePlan& plan, int B, const TypicalAccept& a,
+                                 hipStream_t stream);
 
 // ------------------------------------------------------------------ attention
 struct AttnShape {

@@ -7,7 +7,10 @@
 //
 // Acceptance (same section): a candidate is accepted when it equals the model's first
 // choice at its parent; the longest accepted branch is kept and the deepest accepted
-// node's own first choice is emitted after it.
+// node's own first choice is emitted after it.  Typical acceptance (same section, for
+// sampling) keeps instead every candidate whose probability under its parent's
+// distribution exceeds a threshold tied to that distribution's entropy; here
+// tau = min(epsilon, delta * exp(-H)) at temperature T.
 #include "common.hpp"
 #include "internal.hpp"
 #include "advance.hpp"
@@ -37,6 +40,35 @@ __global__ __launch_bounds__(256) void build_tree_kernel(DevicePlan plan, int K,
 
 constexpr int kAcceptThreads = 1024;
 constexpr int kMaxNodes = MEDUSA_MAX_NODES;
+
+// The kept branch: the deepest accepted node, the lowest index among equals (atomicMax on
+// (depth, -index)); its path root-first, the candidates on it, then the node's argmax.
+// s_acc must be final and visible to every thread; s_best starts at 0.
+__device__ __forceinline__ void emit_branch(const DevicePlan& plan, int b,
+                                            const unsigned char* s_acc, const int* s_arg,
+                                            const int32_t* tok, int& s_best, int32_t* accept_len,
+                                            int32_t* accept_nodes, int32_t* accept_tokens) {
+    const int N = plan.n_nodes;
+    const int D = plan.max_depth;
+    for (int i = threadIdx.x; i < N; i += kAcceptThreads)
+        if (s_acc[i]) atomicMax(&s_best, (plan.depth[i] << 16) | (0xFFFF - i));
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int best = 0xFFFF - (s_best & 0xFFFF);
+        const int a = plan.depth[best];
+        accept_len[b] = a;
+        int32_t* an = accept_nodes + (long long)b * (D + 1);
+        int32_t* at = accept_tokens + (long long)b * (D + 1);
+        for (int j = a + 1; j <= D; ++j) { an[j] = -1; at[j] = -1; }
+        int node = best;
+        for (int j = a; j >= 0; --j) {
+            an[j] = node;
+            if (j >= 1) at[j - 1] = tok[node];
+            node = plan.parent[node];
+        }
+        at[a] = s_arg[best];
+    }
+}
 
 // One workgroup per sequence: merge the lm_head argmax partials of every node, then walk
 // the tree level by level.
@@ -94,25 +126,94 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
         }
         __syncthreads();
     }
-    // deepest accepted node (unique: siblings carry distinct tokens); lowest index on ties
-    for (int i = threadIdx.x; i < N; i += kAcceptThreads)
-        if (s_acc[i]) atomicMax(&s_best, (plan.depth[i] << 16) | (0xFFFF - i));
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int best = 0xFFFF - (s_best & 0xFFFF);
-        const int a = plan.depth[best];
-        accept_len[b] = a;
-        int32_t* an = accept_nodes + (long long)b * (D + 1);
-        int32_t* at = accept_tokens + (long long)b * (D + 1);
-        for (int j = a + 1; j <= D; ++j) { an[j] = -1; at[j] = -1; }
-        int node = best;
-        for (int j = a; j >= 0; --j) {
-            an[j] = node;
-            if (j >= 1) at[j - 1] = tok[node];
-            node = plan.parent[node];
+    emit_branch(plan, b, s_acc, s_arg, tok, s_best, accept_len, accept_nodes, accept_tokens);
+}
+
+// Per node: argmax, the softmax normaliser and the entropy merged over the lm_head tiles,
+// and the threshold; per candidate: its probability under the parent's distribution; then
+// the level walk.  One workgroup per sequence, 16 lanes per node for the merges.
+__global__ __launch_bounds__(kAcceptThreads) void typical_accept_kernel(DevicePlan plan,
+                                                                        TypicalAccept a) {
+    __shared__ int s_arg[kMaxNodes];
+    __shared__ float s_max[kMaxNodes];
+    __shared__ float s_z[kMaxNodes];
+    __shared__ float s_tau[kMaxNodes];
+    __shared__ float s_prob[kMaxNodes];
+    __shared__ unsigned char s_acc[kMaxNodes];
+    __shared__ int s_best;
+    constexpr float kLog2e = 1.4426950408889634f;
+    constexpr int kPerNode = 16;
+    const int b = blockIdx.x;
+    const int N = plan.n_nodes;
+    const int D = plan.max_depth;
+    const int nt = a.n_tiles;
+    for (int i0 = 0; i0 < N; i0 += kAcceptThreads / kPerNode) {
+        const int i = i0 + threadIdx.x / kPerNode;
+        const int sub = threadIdx.x % kPerNode;
+        const long long base = ((long long)b * N + min(i, N - 1)) * nt;
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        for (int t0 = sub; t0 < nt; t0 += 8 * kPerNode) {
+            float v[8];
+            int id[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = t0 + j * kPerNode;
+                v[j] = t < nt ? a.part_val[base + t] : -INFINITY;
+                id[j] = t < nt ? a.part_idx[base + t] : INT_MAX;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
         }
-        at[a] = s_arg[best];
+        row_best(bv, bi);       // every lane of the node's row: the maximum and its id
+        // the tiles' sums rescaled to the node's maximum: with y = (tile max - max) / T,
+        // Z = sum z e^y and S = sum e^y (s + z y), so that H = ln Z - S / Z
+        float z = 0.f, sx = 0.f;
+        for (int t = sub; t < nt; t += kPerNode) {
+            const float y = (a.part_val[base + t] - bv) * a.inv_t;
+            const float g = __builtin_amdgcn_exp2f(y * kLog2e);
+            const float zt = a.part_z[base + t];
+            z += g * zt;
+            sx += g * (a.part_s[base + t] + zt * y);
+        }
+        z = row_sum16(z);
+        sx = row_sum16(sx);
+        if (sub == 0 && i < N) {
+            const float H = logf(z) - sx / z;
+            const float tau = fminf(a.epsilon, a.delta * expf(-H));
+            s_arg[i] = bi;
+            s_max[i] = bv;
+            s_z[i] = z;
+            s_tau[i] = tau;
+            if (a.node_argmax) a.node_argmax[(long long)b * N + i] = bi;
+            if (a.node_tau) a.node_tau[(long long)b * N + i] = tau;
+        }
     }
+    if (threadIdx.x == 0) s_best = 0;
+    __syncthreads();
+    for (int c = threadIdx.x; c < N; c += kAcceptThreads) {
+        float p = 1.f;
+        if (c > 0) {
+            const int par = plan.parent[c];
+            const float y = (a.cand_logit[(long long)b * N + c] - s_max[par]) * a.inv_t;
+            p = __builtin_amdgcn_exp2f(y * kLog2e) / s_z[par];
+        }
+        s_prob[c] = p;
+        s_acc[c] = c == 0;
+        if (a.node_prob) a.node_prob[(long long)b * N + c] = p;
+    }
+    __syncthreads();
+    for (int d = 1; d <= D; ++d) {
+        for (int i = threadIdx.x; i < N; i += kAcceptThreads) {
+            if (plan.depth[i] != d) continue;
+            const int par = plan.parent[i];
+            s_acc[i] = s_acc[par] && s_prob[i] > s_tau[par];
+        }
+        __syncthreads();
+    }
+    emit_branch(plan, b, s_acc, s_arg, a.node_tokens + (long long)b * N, s_best, a.accept_len,
+                a.accept_nodes, a.accept_tokens);
 }
 
 // Next round (same section: the longest accepted branch is kept and its last hidden state
@@ -156,6 +257,12 @@ __global__ __launch_bounds__(256) void advance_kernel(AdvanceArgs a) {
 }
 
 }  // namespace
+
+hipError_t typical_accept_launch(const DevicePlan& plan, int B, const TypicalAccept& a,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(typical_accept_kernel, dim3(B), dim3(kAcceptThreads), 0, stream, plan, a);
+    return hipGetLastError();
+}
 
 hipError_t advance_launch(const AdvanceArgs& args, int B, hipStream_t stream) {
     hipLaunchKernelGGL(advance_kernel, dim3(B), dim3(256), 0, stream, args);

@@ -264,6 +264,28 @@ def medusa_verify_accept(plan: TreePlan, dt, B, H, V, node_hidden, w_lm, node_to
     _check("medusa_verify_accept", st)
 
 
+def medusa_verify_typical_workspace(plan: TreePlan, dt, B, H, V) -> int:
+    return int(lib().medusa_verify_typical_workspace(plan.handle, _dt(dt), B, H, V))
+
+
+def medusa_verify_accept_typical(plan: TreePlan, dt, B, H, V, node_hidden, w_lm, node_tokens,
+                                 temperature, epsilon, delta, node_argmax, node_prob, node_tau,
+                                 accept_len, accept_nodes, accept_tokens, logits=None, ws=None,
+                                 stream=None):
+    torch = _torch()
+    st = lib().medusa_verify_accept_typical(
+        plan.handle, _dt(dt), B, H, V, _float_ptr(node_hidden, dt, "node_hidden"),
+        _float_ptr(w_lm, dt, "w_lm"), _ptr(node_tokens, torch.int32, "node_tokens"),
+        float(temperature), float(epsilon), float(delta),
+        _ptr(node_argmax, torch.int32, "node_argmax"), _ptr(node_prob, torch.float32, "node_prob"),
+        _ptr(node_tau, torch.float32, "node_tau"), _ptr(accept_len, torch.int32, "accept_len"),
+        _ptr(accept_nodes, torch.int32, "accept_nodes"),
+        _ptr(accept_tokens, torch.int32, "accept_tokens"), _ptr(logits, torch.float32, "logits"),
+        _ptr(ws, None, "ws"), ws.numel() * ws.element_size() if ws is not None else 0,
+        _stream(stream))
+    _check("medusa_verify_accept_typical", st)
+
+
 def medusa_proxy_workspace(dt, M, H, Hq, Hkv, d) -> int:
     return int(lib().medusa_proxy_workspace(_dt(dt), M, H, Hq, Hkv, d))
 

@@ -62,10 +62,14 @@ class Dims:
 
 
 class MedusaStep:
+    """``typical``: None for greedy acceptance, or (temperature, epsilon, delta) for typical
+    acceptance (medusa_verify_accept_typical)."""
+
     def __init__(self, dims: Dims, w: Dict[str, "object"], plan: M.TreePlan, device="cuda",
-                 keep_logits: bool = False):
+                 keep_logits: bool = False, typical: Optional[Sequence[float]] = None):
         torch = _torch()
         self.dims, self.w, self.plan = dims, w, plan
+        self.typical = None if typical is None else tuple(float(x) for x in typical)
         n, D, _ = plan.info()
         self.N, self.D = n, D
         dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
@@ -94,7 +98,14 @@ class MedusaStep:
         self.ws_heads = torch.empty(M.medusa_heads_workspace(dims.dtype, B, H, V, K, s_max), **u8)
         self.ws_attn = torch.empty(M.medusa_attention_workspace(plan, dims.dtype, B, dims.Hq,
                                                                 dims.Hkv, dims.d, dims.Lcap), **u8)
-        self.ws_verify = torch.empty(M.medusa_verify_workspace(plan, dims.dtype, B, H, V), **u8)
+        if self.typical is None:
+            self.node_prob = self.node_tau = None
+            self.ws_verify = torch.empty(M.medusa_verify_workspace(plan, dims.dtype, B, H, V), **u8)
+        else:
+            self.node_prob = torch.empty(B, n, **f32)
+            self.node_tau = torch.empty(B, n, **f32)
+            self.ws_verify = torch.empty(M.medusa_verify_typical_workspace(plan, dims.dtype, B, H, V),
+                                         **u8)
         self.ws_proxy = torch.empty(M.medusa_proxy_workspace(dims.dtype, B * n, H, dims.Hq,
                                                              dims.Hkv, dims.d), **u8)
 
@@ -130,6 +141,14 @@ class MedusaStep:
 
     def verify(self):
         d, w = self.dims, self.w
+        if self.typical is not None:
+            T, eps, delta = self.typical
+            M.medusa_verify_accept_typical(self.plan, d.dtype, d.B, d.H, d.V, self.node_hidden,
+                                           w["w_lm"], self.node_tokens, T, eps, delta,
+                                           self.node_argmax, self.node_prob, self.node_tau,
+                                           self.accept_len, self.accept_nodes, self.accept_tokens,
+                                           self.verify_logits, self.ws_verify)
+            return
         M.medusa_verify_accept(self.plan, d.dtype, d.B, d.H, d.V, self.node_hidden, w["w_lm"],
                                self.node_tokens, self.node_argmax, self.accept_len,
                                self.accept_nodes, self.accept_tokens, self.verify_logits,
@@ -198,5 +217,6 @@ class MedusaStep:
 
         names = ["topk_ids", "topk_vals", "root_ids", "u", "node_tokens", "position_ids", "q",
                  "k_tree", "v_tree", "o", "node_hidden", "node_argmax", "accept_len",
-                 "accept_nodes", "accept_tokens", "head_logits", "verify_logits"]
+                 "accept_nodes", "accept_tokens", "head_logits", "verify_logits", "node_prob",
+                 "node_tau"]
         return {n: host(getattr(self, n)) for n in names}

@@ -78,12 +78,12 @@ def gpu_plan(inp, device):
 
 
 def run_gpu(inp, device, keep_logits=True, bootstrap_root=True, root=None, keep_u=True,
-            plan=None):
+            plan=None, typical=None):
     import torch
     from speculative_decoding_amd.step import Dims, MedusaStep, device_weights
     plan = gpu_plan(inp, device) if plan is None else plan.upload(device)
     step = MedusaStep(Dims.from_config(inp.cfg), device_weights(inp, device), plan, device,
-                      keep_logits=keep_logits)
+                      keep_logits=keep_logits, typical=typical)
     if root is not None:
         step.root_ids.copy_(torch.as_tensor(np.asarray(root, np.int32), device=device))
     step.run(bootstrap_root=bootstrap_root, keep_u=keep_u)

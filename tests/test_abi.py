@@ -174,3 +174,22 @@ def test_advance_error_paths():
     assert _advance(L, plan, kc=FAKE + 8) == 2           # misaligned
     assert _advance(L, plan, hout=FAKE) == 2             # next h overlaps node_hidden
     assert _advance(L, plan, Lcap=0) == 2
+
+
+def test_typical_error_paths():
+    from speculative_decoding_amd import medusa as M
+    plan = M.medusa_tree_plan_full((2, 3))
+    L = lib()
+    ws = M.medusa_verify_typical_workspace(plan, "bf16", 2, 256, 1000)
+    assert ws > M.medusa_verify_workspace(plan, "bf16", 2, 256, 1000) > 0
+    null = None
+    # null outputs
+    st = L.medusa_verify_accept_typical(plan.handle, 1, 1, 256, 1000, 16, 16, 16, 1.0, 0.1, 0.1,
+                                        null, null, null, null, 16, 16, null, 16, ws, null)
+    assert st == 1
+    # temperature, epsilon, delta out of range (checked before any device access)
+    for T, e, d in ((0.0, 0.1, 0.1), (1e-7, 0.1, 0.1), (float("nan"), 0.1, 0.1),
+                    (1.0, -0.1, 0.1), (1.0, 0.1, float("inf")), (1.0, float("nan"), 0.1)):
+        st = L.medusa_verify_accept_typical(plan.handle, 1, 1, 256, 1000, 16, 16, 16, T, e, d,
+                                            null, null, null, 16, 16, 16, null, 16, ws, null)
+        assert st == 2, (T, e, d, st)

@@ -1,0 +1,130 @@
+"""GPU parity of typical acceptance (medusa_verify_accept_typical) against the oracle's
+typical_accept, on planted inputs (every node's argmax has a margin, so node tokens and
+argmax are exact).  Each candidate's probability under its parent's distribution and each
+node's threshold are fp32 on the device and within tolerance of the oracle's fp64; the
+accept results must be exactly what the walk makes of the device's own probabilities and
+thresholds, and equal the oracle's wherever no decision on the way sits within the
+tolerance of its threshold.  At a temperature near zero the result is greedy acceptance
+bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import close, exact, oracle_plan, planted, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+PROB_RTOL = 2e-2
+PROB_ATOL = 1e-30
+
+# (config, seed, temperature, epsilon, delta); configurations cover the fp32 kernel (tiny),
+# the row-streaming kernel (up to 64 rows), the slab kernel (more than 64 rows), several
+# sequences, flat (T = 1) and sharp (small T) distributions
+CASES = [
+    ("tiny", 0, 1.0, 0.3, 0.09),
+    ("tiny", 2, 0.2, 0.09, 0.3),
+    ("small", 0, 1.0, 0.09, 0.3),
+    ("small", 1, 0.05, 0.09, 0.3),
+    ("small_batched", 0, 0.5, 0.2, 0.5),
+    ("small_dense", 0, 1.0, 0.09, 0.3),
+    ("small_n341", 0, 0.7, 0.05, 0.5),
+]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from speculative_decoding_amd import lib
+    lib()
+    return torch.device("cuda:0")
+
+
+def _check_typical(inp, got, ref, plan, T, eps, delta):
+    a, nodes, toks, prob, tau = oracle.typical_accept(plan, ref.tokens, ref.logits,
+                                                      ref.node_argmax, T, eps, delta)
+    exact("root_ids", got["root_ids"], ref.root)
+    exact("node_tokens", got["node_tokens"], ref.tokens)
+    exact("node_argmax", got["node_argmax"], ref.node_argmax)
+    close("node_hidden", got["node_hidden"], ref.node_hidden)
+    close("node_prob", got["node_prob"], prob, rtol=PROB_RTOL, atol=PROB_ATOL)
+    close("node_tau", got["node_tau"], tau, rtol=PROB_RTOL, atol=PROB_ATOL)
+    # the device's walk over its own probabilities and thresholds
+    ga, gn, gt = oracle.typical_branch(plan, got["node_tokens"], got["node_argmax"],
+                                       got["node_prob"].astype(np.float64),
+                                       got["node_tau"].astype(np.float64))
+    exact("accept_len (device rule)", got["accept_len"], ga)
+    exact("accept_nodes (device rule)", got["accept_nodes"], gn)
+    exact("accept_tokens (device rule)", got["accept_tokens"], gt)
+    # and the oracle's decisions, where none is within tolerance of its threshold
+    B, N = ref.tokens.shape
+    close_calls = 0
+    for b in range(B):
+        for i in range(1, N):
+            par = int(plan.parent[i])
+            if abs(prob[b, i] - tau[b, par]) <= PROB_RTOL * max(prob[b, i], tau[b, par]):
+                close_calls += 1
+    if close_calls == 0:
+        exact("accept_len", got["accept_len"], a)
+        exact("accept_nodes", got["accept_nodes"], nodes)
+        exact("accept_tokens", got["accept_tokens"], toks)
+    say(f"    accept {got['accept_len'].tolist()} (oracle {a.tolist()}), "
+        f"{close_calls} decisions within tolerance of the threshold")
+
+
+@pytest.mark.parametrize("cfg,seed,T,eps,delta", CASES)
+def test_typical_step(dev, cfg, seed, T, eps, delta):
+    say(f"[typical {cfg} seed {seed} T={T} eps={eps} delta={delta}]")
+    inp = planted(cfg, seed)
+    plan = oracle_plan(inp)
+    ref = oracle.step(inp, plan)
+    _, got = run_gpu(inp, dev, typical=(T, eps, delta))
+    _check_typical(inp, got, ref, plan, T, eps, delta)
+    close("verify_logits", got["verify_logits"], ref.logits, row_scale=True)
+
+
+@pytest.mark.parametrize("cfg,seed", [("tiny", 1), ("small", 0), ("small_batched", 1),
+                                      ("small_dense", 1)])
+def test_typical_low_temperature_is_greedy(dev, cfg, seed):
+    """T = 1e-4 with planted margins >= 1e-2: only the argmax keeps any probability, so
+    typical acceptance makes exactly the greedy decisions."""
+    say(f"[typical T=1e-4 {cfg} seed {seed}]")
+    inp = planted(cfg, seed)
+    _, greedy = run_gpu(inp, dev, keep_logits=False)
+    _, typ = run_gpu(inp, dev, keep_logits=False, typical=(1e-4, 0.09, 0.3))
+    for name in ("node_argmax", "accept_len", "accept_nodes", "accept_tokens"):
+        exact(name, typ[name], greedy[name])
+    assert set(np.unique(typ["node_prob"]).tolist()) <= {0.0, 1.0} or \
+        np.all((typ["node_prob"] < 1e-30) | (typ["node_prob"] > 1 - 1e-6))
+
+
+def test_typical_run_twice_bitwise(dev):
+    import torch
+    inp = planted("small_dense", 0)
+    step, first = run_gpu(inp, dev, keep_logits=False, typical=(0.7, 0.09, 0.3))
+    step.run(bootstrap_root=True)
+    torch.cuda.synchronize()
+    second = step.results()
+    for name in ("node_prob", "node_tau"):
+        assert np.array_equal(first[name].view(np.uint32), second[name].view(np.uint32)), name
+    for name in ("accept_len", "accept_nodes", "accept_tokens", "node_argmax"):
+        exact(name, second[name], first[name])
+
+
+@pytest.mark.slow
+def test_typical_8b(dev):
+    import os
+    import torch
+    from tests.gpu_util import PLANTS
+    if not os.path.exists(os.path.join(PLANTS, "8b_s0.json")):
+        pytest.skip("no stored plant for 8b seed 0")
+    say("[typical 8b seed 0] generating")
+    inp = planted("8b", 0)
+    plan = oracle_plan(inp)
+    say("[typical 8b seed 0] gpu step")
+    step, got = run_gpu(inp, dev, keep_logits=False, keep_u=False, typical=(0.5, 0.09, 0.3))
+    del step
+    torch.cuda.empty_cache()
+    say("[typical 8b seed 0] oracle step")
+    ref = oracle.step(inp, plan)
+    _check_typical(inp, got, ref, plan, 0.5, 0.09, 0.3)
