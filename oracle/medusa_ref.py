@@ -21,8 +21,10 @@ Steps and the passages they follow:
   node 0 carries the base model's own next token.
 * ``proxy_qkv``, ``proxy_out`` — the one-layer stand-in for the frozen base
   model that scores the tree (embedding gather, Q/K/V projections, attention
-  output projection with residual).  Not part of the method; no norm, MLP,
-  bias or positional encoding.
+  output projection with residual).  Not part of the method; no norm, MLP or
+  bias.  Optionally ``rope`` rotates q and k by position (positions L + depth,
+  siblings sharing one); the pages say nothing of positions, so this is the
+  common rotary form of decoder layers, off unless a base is given.
 * ``tree_attention``  — same section: all candidates are appended at once and
   a mask lets each token see only its tree ancestors (read: ancestors and
   itself) on top of the KV prefix.
@@ -61,7 +63,7 @@ __all__ = [
     "as_f64", "round_act", "silu", "matvec_rows", "heads_forward", "lm_head_logits", "topk",
     "argmax_lowest", "build_tree", "proxy_qkv", "tree_attention", "proxy_out", "verify",
     "accept", "greedy_decode", "StepResult", "step", "causal_attention_last", "store_act",
-    "advance", "decode_loop", "softmax_entropy", "typical_accept", "typical_branch",
+    "advance", "decode_loop", "softmax_entropy", "typical_accept", "typical_branch", "rope",
 ]
 
 _CHUNK_ROWS = 8192
@@ -204,14 +206,38 @@ def build_tree(plan: TreePlan, root_ids: np.ndarray, topk_ids: np.ndarray,
 
 # ----------------------------------------------------------------- verifier layer
 
-def proxy_qkv(tokens: np.ndarray, embed, wq, wk, wv, Hq: int, Hkv: int, d: int, dtype: str):
-    """x_i = E[token_i]; q = rnd(Wq x), k = rnd(Wk x), v = rnd(Wv x).
+def rope(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarray:
+    """Rotary position embedding over the last axis (head dimension d, even), pairing
+    element i with element i + d/2: for i < d/2, theta_i = base^(-2i/d) and
+    angle = position * theta_i,
+        y_i       = x_i cos(angle) - x_{i+d/2} sin(angle)
+        y_{i+d/2} = x_{i+d/2} cos(angle) + x_i sin(angle).
+    x [..., heads, d]; positions has x's shape without the last two axes."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    theta = np.power(float(base), -2.0 * np.arange(h, dtype=np.float64) / d)
+    ang = np.asarray(positions, dtype=np.float64)[..., None, None] * theta     # [..., 1, h]
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :h], x[..., h:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def proxy_qkv(tokens: np.ndarray, embed, wq, wk, wv, Hq: int, Hkv: int, d: int, dtype: str,
+              positions: Optional[np.ndarray] = None, rope_base: float = 0.0):
+    """x_i = E[token_i]; q = rnd(Wq x), k = rnd(Wk x), v = rnd(Wv x); with rope_base > 0,
+    q and k are then rotated by their positions and rounded again (the projections'
+    stored outputs are what the rotation reads).
     tokens [B, N] -> x [B,N,H], q [B,N,Hq,d], k/v [B,N,Hkv,d] (float64)."""
     B, N = tokens.shape
     x = as_f64(embed[tokens.reshape(-1)], dtype)                       # [B*N, H]
     q = round_act(matvec_rows(wq, x.T, dtype).T, dtype).reshape(B, N, Hq, d)
     k = round_act(matvec_rows(wk, x.T, dtype).T, dtype).reshape(B, N, Hkv, d)
     v = round_act(matvec_rows(wv, x.T, dtype).T, dtype).reshape(B, N, Hkv, d)
+    if rope_base > 0.0:
+        pos = np.asarray(positions).reshape(B, N)
+        q = round_act(rope(q, pos, rope_base), dtype)
+        k = round_act(rope(k, pos, rope_base), dtype)
     return x.reshape(B, N, -1), q, k, v
 
 
@@ -316,8 +342,10 @@ def greedy_decode(inp, b: int, first_token: int, n_tokens: int):
     """Plain greedy decoding with the one-layer verifier, one token at a time.
 
     The cache starts as the prefix of sequence b.  For each step: x = E[tok],
-    q/k/v projected and rounded, (k, v) appended to the cache, attention over
-    the whole cache, hidden = rnd(x + Wo o), next = argmax(lm_head(hidden)).
+    q/k/v projected and rounded (and q, k rotated to the token's position L + j
+    when the workload has a rotary base), (k, v) appended to the cache,
+    attention over the whole cache, hidden = rnd(x + Wo o),
+    next = argmax(lm_head(hidden)).
     Returns (tokens [n_tokens], hiddens [n_tokens, H], logits [n_tokens, V])
     generated after ``first_token``."""
     cfg = inp.cfg
@@ -328,11 +356,15 @@ def greedy_decode(inp, b: int, first_token: int, n_tokens: int):
     scale = 1.0 / np.sqrt(cfg.d)
     tok = int(first_token)
     out_t, out_h, out_l = [], [], []
-    for _ in range(n_tokens):
+    base = float(getattr(cfg, "rope_base", 0.0))
+    for j in range(n_tokens):
         x = as_f64(inp.embed[tok], dt)
         q = round_act(matvec_rows(inp.wq, x, dt), dt).reshape(cfg.Hq, cfg.d)
         k = round_act(matvec_rows(inp.wk, x, dt), dt).reshape(1, cfg.Hkv, cfg.d)
         v = round_act(matvec_rows(inp.wv, x, dt), dt).reshape(1, cfg.Hkv, cfg.d)
+        if base > 0.0:
+            q = round_act(rope(q, np.array(L + j), base), dt)
+            k = round_act(rope(k, np.array([L + j]), base), dt)
         keys = np.concatenate([keys, k], axis=0)
         vals = np.concatenate([vals, v], axis=0)
         o = round_act(causal_attention_last(q, keys, vals, cfg.Hq, cfg.Hkv, scale), dt)
@@ -384,7 +416,8 @@ def step(inp, plan: TreePlan, root: Optional[np.ndarray] = None) -> StepResult:
         root = np.array([argmax_lowest(root_logits[b]) for b in range(cfg.B)], dtype=np.int64)
     hl, ids, vals, u = heads_forward(inp.h, inp.w1, inp.b1, inp.w2, cfg.s, dt)
     tokens, pos = build_tree(plan, root, ids, inp.prefix_lens)
-    x, q, k, v = proxy_qkv(tokens, inp.embed, inp.wq, inp.wk, inp.wv, cfg.Hq, cfg.Hkv, cfg.d, dt)
+    x, q, k, v = proxy_qkv(tokens, inp.embed, inp.wq, inp.wk, inp.wv, cfg.Hq, cfg.Hkv, cfg.d, dt,
+                           positions=pos, rope_base=float(getattr(cfg, "rope_base", 0.0)))
     o = tree_attention(plan, q, k, v, inp.k_cache, inp.v_cache, inp.prefix_lens, dt)
     nh = proxy_out(x, o, inp.wo, dt)
     logits, am = verify(nh, inp.w_lm, dt)

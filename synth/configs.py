@@ -55,6 +55,7 @@ class Config:
     sigma_embed: float = 1.0    # token embedding table E
     sigma_h: float = 1.0        # last hidden state
     sigma_kv: float = 1.0       # cached K/V prefix
+    rope_base: float = 0.0      # rotary position embedding base of the verifier (0: none)
     note: str = field(default="", compare=False)
 
     @property
@@ -141,6 +142,18 @@ CONFIGS = {
         tree_s=(10, 5, 4, 3), n_nodes=341, Hq=8, Hkv=2, d=128, L=300, Lcap=320,
         sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
         sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
+    # the verifier with rotary positions (base 10000): ragged prefixes including an empty
+    # one, and a loop case whose rounds move the positions on
+    "small_rope": Config(
+        name="small_rope", B=3, H=512, V=3001, K=3, s=(4, 3, 2), tree="sparse",
+        tree_s=(4, 3, 2), n_nodes=16, Hq=4, Hkv=1, d=64, lens=(0, 129, 300), Lcap=300,
+        sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
+        sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512), rope_base=10000.0),
+    "small_rope_loop": Config(
+        name="small_rope_loop", B=2, H=512, V=3001, K=3, s=(4, 3, 2), tree="sparse",
+        tree_s=(4, 3, 2), n_nodes=16, Hq=4, Hkv=2, d=128, lens=(40, 97), Lcap=160,
+        sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
+        sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512), rope_base=10000.0),
     # decode-loop cases: room in the KV cache for several rounds of accepted branches
     "tiny_loop": Config(
         name="tiny_loop", B=1, H=256, V=1000, K=3, s=(2, 3, 3), tree="full", tree_s=(2, 3),

@@ -322,7 +322,9 @@ def test_accept_hand_cases():
 
 
 @pytest.mark.parametrize("cfg,seed", [("tiny", s) for s in range(6)] + [("small_batched", 0),
-                                                                         ("small", 1)])
+                                                                         ("small", 1),
+                                                                         ("small_rope", 0),
+                                                                         ("small_rope", 2)])
 def test_step_equals_greedy_decoding(cfg, seed):
     """Emitted tokens equal plain greedy decoding with the same verifier, and the accepted
     length is maximal ("Medusa Decoding Heads", section "Diepe duik")."""
@@ -341,7 +343,8 @@ def test_step_equals_greedy_decoding(cfg, seed):
 
 
 @pytest.mark.parametrize("cfg,seed", [("tiny_loop", 0), ("tiny_loop", 2), ("small_loop", 1),
-                                      ("small_loop", 3)])
+                                      ("small_loop", 3), ("small_rope_loop", 0),
+                                      ("small_rope_loop", 1)])
 def test_decode_loop_equals_greedy_decoding(cfg, seed):
     """Several rounds, each keeping the longest accepted branch and feeding its last
     hidden state to the heads (glossary "Medusa Heads", section "Attention arborescente
@@ -368,7 +371,9 @@ def test_decode_loop_equals_greedy_decoding(cfg, seed):
             assert np.array_equal(cur_next.v_cache[b, :L], cur.v_cache[b, :L])
             toks = [int(r.tokens[b, 0])] + [int(t) for t in r.accept_tokens[b, :a]]
             _, _, k_ref, v_ref = oracle.proxy_qkv(np.array([toks]), inp.embed, inp.wq, inp.wk, inp.wv,
-                                                  inp.cfg.Hq, inp.cfg.Hkv, inp.cfg.d, inp.dtype)
+                                                  inp.cfg.Hq, inp.cfg.Hkv, inp.cfg.d, inp.dtype,
+                                                  positions=np.arange(L, L + a + 1)[None],
+                                                  rope_base=inp.cfg.rope_base)
             got_k = oracle.as_f64(cur_next.k_cache[b, L: L + a + 1], inp.dtype)
             got_v = oracle.as_f64(cur_next.v_cache[b, L: L + a + 1], inp.dtype)
             assert np.array_equal(got_k, k_ref[0]) and np.array_equal(got_v, v_ref[0])
@@ -505,3 +510,46 @@ def test_typical_higher_threshold_never_accepts_more():
         if prev is not None:
             assert (a <= prev).all()
         prev = a
+
+
+# ------------------------------------------------------------------ rotary positions
+
+def test_rope_closed_forms():
+    base, d, p = 10000.0, 8, 7.0
+    x = np.zeros((1, d))
+    # position 0 is the identity
+    g = np.random.default_rng(3).normal(size=(2, 3, d))
+    assert np.array_equal(oracle.rope(g, np.zeros(2), base), g)
+    # a unit vector at i < d/2 turns towards i + d/2 by p * base^(-2i/d), and back from there
+    for i in range(d // 2):
+        th = p * base ** (-2.0 * i / d)
+        e = x.copy()
+        e[0, i] = 1.0
+        y = oracle.rope(e, np.array(p), base)[0]
+        want = np.zeros(d)
+        want[i], want[i + d // 2] = math.cos(th), math.sin(th)
+        np.testing.assert_allclose(y, want, rtol=0, atol=1e-15)
+        e = x.copy()
+        e[0, i + d // 2] = 1.0
+        y = oracle.rope(e, np.array(p), base)[0]
+        want = np.zeros(d)
+        want[i], want[i + d // 2] = -math.sin(th), math.cos(th)
+        np.testing.assert_allclose(y, want, rtol=0, atol=1e-15)
+    # d = 2: the plane rotation by the position itself (theta_0 = 1)
+    v = np.array([[0.3, -1.7]])
+    y = oracle.rope(v, np.array(2.5), base)[0]
+    c, s = math.cos(2.5), math.sin(2.5)
+    np.testing.assert_allclose(y, [0.3 * c + 1.7 * s, -1.7 * c + 0.3 * s], rtol=1e-15)
+
+
+def test_rope_depends_on_relative_position_only():
+    g = np.random.default_rng(5)
+    q = g.normal(size=(4, 64))
+    k = g.normal(size=(4, 64))
+    for m, n, shift in ((3, 0, 1000), (100, 97, 12345), (0, 4096, 7)):
+        a = (oracle.rope(q, np.array(m), 10000.0) * oracle.rope(k, np.array(n), 10000.0)).sum(-1)
+        b = (oracle.rope(q, np.array(m + shift), 10000.0) *
+             oracle.rope(k, np.array(n + shift), 10000.0)).sum(-1)
+        np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-9)
+        np.testing.assert_allclose(np.linalg.norm(oracle.rope(q, np.array(m), 10000.0), axis=-1),
+                                   np.linalg.norm(q, axis=-1), rtol=1e-13)
