@@ -187,6 +187,35 @@ def typical_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, steps: int, warm
     return out
 
 
+ROPE_BASE = 10000.0
+
+
+def rope_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, steps: int, warmup: int):
+    """Whole steps with rotary positions on the verifier's q and k (medusa_rope after the
+    projections), on the same inputs and plan; then a pass with the rotation event-timed."""
+    import dataclasses
+    st = MedusaStep(dataclasses.replace(Dims.from_config(cfg), rope_base=ROPE_BASE), w, plan, dev)
+    st.heads(bootstrap_root=True)
+    for _ in range(warmup):
+        st.run(bootstrap_root=False, keep_u=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.run(bootstrap_root=False, keep_u=False)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    M.medusa_profile_reset()
+    M.medusa_profile_only("rope")
+    M.medusa_profile_enable(True)
+    for _ in range(steps):
+        st.run(bootstrap_root=False, keep_u=False)
+    torch.cuda.synchronize()
+    M.medusa_profile_enable(False)
+    ms, n = M.medusa_profile_query("rope")
+    return {"base": ROPE_BASE, "steps": steps, "ms_per_step": 1e3 * sec, "steps_per_s": 1.0 / sec,
+            "rope_us": 1e3 * ms / n if n else None}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -266,7 +295,8 @@ def main() -> int:
                          "after the main measurement (empty: skip)")
     ap.add_argument("--sweep-steps", type=int, default=40)
     ap.add_argument("--typical-steps", type=int, default=100,
-                    help="whole steps timed with typical acceptance (0: skip)")
+                    help="whole steps timed with typical acceptance, and again with rotary "
+                         "positions (0: skip both)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run an elementwise kernel that reads and writes this many MiB once before "
                          "the timed region (known sizes to calibrate rocprofv3 byte counters)")
@@ -358,6 +388,11 @@ def main() -> int:
         log("[bench] typical acceptance")
         typical = typical_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, args.typical_steps,
                                max(3, args.typical_steps // 10))
+    rope = None
+    if args.typical_steps > 0:
+        log("[bench] rotary positions")
+        rope = rope_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, args.typical_steps,
+                         max(3, args.typical_steps // 10))
     sweep = None
     counts = [int(x) for x in args.sweep_nodes.split(",") if x.strip()]
     if counts:
@@ -409,6 +444,7 @@ def main() -> int:
         "decode_loop": loop,
         "node_sweep": sweep,
         "typical": typical,
+        "rope": rope,
         "device": device,
         "kernels_note": "per-kernel averages from a second pass of the same steps with every "
                         "launch event-timed (not the timed region)",

@@ -265,6 +265,17 @@ medusa_status medusa_proxy_qkv(medusa_dtype dt, int M, int H, int V, int Hq, int
                                const int32_t* tokens, const void* embed, const void* wq,
                                const void* wk, const void* wv, void* q, void* k, void* v,
                                void* ws, size_t ws_bytes, void* stream);
+/* Rotary positions for the verifier's q and k, in place (not on the pages; a real decoder
+ * layer needs it): with element i of a head paired with element i + d/2, for i < d/2,
+ *     theta_i = base^(-2i/d),  a = positions[m] * theta_i,
+ *     (x_i, x_{i+d/2}) <- (x_i cos a - x_{i+d/2} sin a,  x_{i+d/2} cos a + x_i sin a),
+ * then rounded to dt once.  Tree nodes take positions[m] = L + depth (position_ids of
+ * medusa_build_tree).  The angle is reduced in fp64, the rotation is fp32.
+ *   q [M, Hq, d] and k [M, Hkv, d] dtype, updated   positions [M] int32.
+ *   d % 8 == 0, 1 < base (finite). */
+medusa_status medusa_rope(medusa_dtype dt, int M, int Hq, int Hkv, int d, const int32_t* positions,
+                          float base, void* q, void* k, void* stream);
+
 medusa_status medusa_proxy_out(medusa_dtype dt, int M, int H, int V, int Hq, int d,
                                const int32_t* tokens, const void* embed, const void* o,
                                const void* wo, void* node_hidden, void* ws, size_t ws_bytes,

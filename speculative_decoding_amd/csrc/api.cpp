@@ -9,6 +9,7 @@
 
 #include "advance.hpp"
 #include "plan_impl.hpp"
+#include "rope.hpp"
 
 using namespace medusa;
 
@@ -438,6 +439,36 @@ medusa_status medusa_verify_accept_typical(const medusa_tree_plan* plan, medusa_
     ta.accept_tokens = accept_tokens;
     prof_begin("verify_accept", strm);
     e = typical_accept_launch(dp, B, ta, strm);
+    prof_end(strm);
+    if (e != hipSuccess) return medusa_internal_hip_error(e);
+    return MEDUSA_OK;
+}
+
+medusa_status medusa_rope(medusa_dtype dt, int M, int Hq, int Hkv, int d, const int32_t* positions,
+                          float base, void* q, void* k, void* stream) {
+    if (!positions || !q || !k) return MEDUSA_ERR_NULL;
+    if (!dtype_ok(dt)) return MEDUSA_ERR_UNSUPPORTED;
+    if (M < 1 || Hq < 1 || Hkv < 1 || d < 8 || d % 8 != 0 || d > 4096 ||
+        (long long)M * (Hq + Hkv) * (d / 8) > (1LL << 31))
+        return MEDUSA_ERR_SHAPE;
+    if (!(base > 1.0f) || !std::isfinite(base)) return MEDUSA_ERR_SHAPE;
+    const size_t align = dt == MEDUSA_BF16 ? 8 : 16;
+    if (reinterpret_cast<uintptr_t>(q) % align || reinterpret_cast<uintptr_t>(k) % align)
+        return MEDUSA_ERR_SHAPE;
+    medusa_status st = medusa_internal_device_check();
+    if (st != MEDUSA_OK) return st;
+    RopeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.positions = positions;
+    a.log2_base = std::log2((double)base);
+    a.M = M;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.d = d;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    prof_begin("rope", strm);
+    hipError_t e = rope_launch(dt, a, strm);
     prof_end(strm);
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     return MEDUSA_OK;

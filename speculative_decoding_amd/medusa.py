@@ -286,6 +286,14 @@ def medusa_verify_accept_typical(plan: TreePlan, dt, B, H, V, node_hidden, w_lm,
     _check("medusa_verify_accept_typical", st)
 
 
+def medusa_rope(dt, M, Hq, Hkv, d, positions, base, q, k, stream=None):
+    torch = _torch()
+    st = lib().medusa_rope(_dt(dt), M, Hq, Hkv, d, _ptr(positions, torch.int32, "positions"),
+                           float(base), _float_ptr(q, dt, "q"), _float_ptr(k, dt, "k"),
+                           _stream(stream))
+    _check("medusa_rope", st)
+
+
 def medusa_proxy_workspace(dt, M, H, Hq, Hkv, d) -> int:
     return int(lib().medusa_proxy_workspace(_dt(dt), M, H, Hq, Hkv, d))
 

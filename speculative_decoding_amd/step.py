@@ -50,6 +50,7 @@ class Dims:
     d: int
     Lcap: int
     dtype: str
+    rope_base: float = 0.0      # rotary positions on the verifier's q and k (0: none)
 
     @property
     def s_max(self) -> int:
@@ -58,7 +59,8 @@ class Dims:
     @classmethod
     def from_config(cls, cfg) -> "Dims":
         return cls(B=cfg.B, H=cfg.H, V=cfg.V, K=cfg.K, s=tuple(cfg.s), Hq=cfg.Hq, Hkv=cfg.Hkv,
-                   d=cfg.d, Lcap=cfg.Lcap, dtype=cfg.dtype)
+                   d=cfg.d, Lcap=cfg.Lcap, dtype=cfg.dtype,
+                   rope_base=float(getattr(cfg, "rope_base", 0.0)))
 
 
 class MedusaStep:
@@ -127,6 +129,9 @@ class MedusaStep:
         M.medusa_proxy_qkv(d.dtype, d.B * self.N, d.H, d.V, d.Hq, d.Hkv, d.d, self.node_tokens,
                            w["embed"], w["wq"], w["wk"], w["wv"], self.q, self.k_tree, self.v_tree,
                            self.ws_proxy)
+        if d.rope_base > 0.0:
+            M.medusa_rope(d.dtype, d.B * self.N, d.Hq, d.Hkv, d.d, self.position_ids, d.rope_base,
+                          self.q, self.k_tree)
 
     def attention(self):
         d, w = self.dims, self.w

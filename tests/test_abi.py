@@ -193,3 +193,16 @@ def test_typical_error_paths():
         st = L.medusa_verify_accept_typical(plan.handle, 1, 1, 256, 1000, 16, 16, 16, T, e, d,
                                             null, null, null, 16, 16, 16, null, 16, ws, null)
         assert st == 2, (T, e, d, st)
+
+
+def test_rope_error_paths():
+    L = lib()
+    # null pointers, then shapes and bases (all checked before any device access)
+    assert L.medusa_rope(1, 4, 2, 1, 64, None, 10000.0, 16, 16, None) == 1
+    assert L.medusa_rope(1, 4, 2, 1, 64, 16, 10000.0, None, 16, None) == 1
+    for M, Hq, Hkv, d, base in ((0, 2, 1, 64, 1e4), (4, 2, 1, 60, 1e4), (4, 2, 1, 4, 1e4),
+                                (4, 0, 1, 64, 1e4), (4, 2, 1, 64, 1.0), (4, 2, 1, 64, float("inf")),
+                                (4, 2, 1, 64, float("nan")), (4, 2, 1, 64, -5.0)):
+        assert L.medusa_rope(1, M, Hq, Hkv, d, 16, base, 16, 16, None) == 2, (M, Hq, Hkv, d, base)
+    # misaligned q for bf16 (8-byte quads)
+    assert L.medusa_rope(1, 4, 2, 1, 64, 16, 1e4, 20, 16, None) == 2

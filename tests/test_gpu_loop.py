@@ -38,7 +38,8 @@ def _gpu_step(inp, dev):
 
 
 @pytest.mark.parametrize("cfg,seed", [("tiny_loop", 0), ("tiny_loop", 2), ("small_loop", 1),
-                                      ("small_loop", 3)])
+                                      ("small_loop", 3), ("small_rope_loop", 2),
+                                      ("small_rope_loop", 5)])
 def test_decode_loop_emits_greedy_stream(dev, cfg, seed):
     import torch
     say(f"[decode loop {cfg} seed {seed}]")
@@ -59,7 +60,7 @@ def test_decode_loop_emits_greedy_stream(dev, cfg, seed):
         exact(f"sequence {b} stream vs the oracle loop", streams[b][:n], ref_streams[b][:n])
 
 
-@pytest.mark.parametrize("cfg,seed", [("small_loop", 3), ("tiny_loop", 0)])
+@pytest.mark.parametrize("cfg,seed", [("small_loop", 3), ("tiny_loop", 0), ("small_rope_loop", 1)])
 def test_advance_matches_oracle(dev, cfg, seed):
     import torch
     say(f"[advance {cfg} seed {seed}]")

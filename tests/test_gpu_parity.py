@@ -35,7 +35,8 @@ def test_tiny_step(dev, seed):
 @pytest.mark.parametrize("cfg,seed", [("small", 0), ("small", 1), ("small", 2),
                                       ("small_batched", 0), ("small_batched", 1),
                                       ("small_dense", 0), ("small_dense", 1),
-                                      ("small_n1", 0), ("small_n341", 0), ("small_n341", 5)])
+                                      ("small_n1", 0), ("small_n341", 0), ("small_n341", 5),
+                                      ("small_rope", 0), ("small_rope", 2)])
 def test_small_step(dev, cfg, seed):
     say(f"[{cfg} seed {seed}]")
     inp = planted(cfg, seed)
