@@ -104,22 +104,24 @@ def decode_loop_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, rounds: int)
                     "mostly accept nothing; every round still emits its bonus token"}
 
 
-SWEEP_DENSE = {4: (3, 4, 4, 4)}     # the dense 256-node tree (1+3+12+48+192) for four heads
+# dense trees for four heads: the full product of top-(3,4,4,4), 1+3+12+48+192 = 256 nodes,
+# and of top-(4,4,4,4), whose 4^4 = 256 leaf paths make 341 nodes
+SWEEP_DENSE = {4: ((3, 4, 4, 4), (4, 4, 4, 4))}
 SWEEP_NODES = "1,16,32,64,128,256,341"
 
 
 def node_sweep(torch, M, MedusaStep, Dims, cfg, w, dev, seed: int, node_counts, steps: int,
                warmup: int):
     """Whole-step time t(N) for sparse trees of N nodes (the most accurate combinations)
-    and for the dense Cartesian tree, on the workload's weights and KV prefix.  E[a](N)
+    and for the dense Cartesian trees, on the workload's weights and KV prefix.  E[a](N)
     comes from the synthetic accuracy table drawn over the union of the trees' ranks; the
     predicted rate is (1 + E[a]) / t(N) per sequence."""
     import dataclasses
     import numpy as np
     from speculative_decoding_amd import budget
     from synth.gen import accuracy_table
-    dense_s = SWEEP_DENSE.get(cfg.K)
-    s = tuple(max(a, b) for a, b in zip(cfg.s, dense_s)) if dense_s else tuple(cfg.s)
+    dense = SWEEP_DENSE.get(cfg.K, ())
+    s = tuple(max([a] + [ds[k] for ds in dense]) for k, a in enumerate(cfg.s))
     scfg = dataclasses.replace(cfg, s=s, tree_s=s)
     acc = accuracy_table(scfg, seed)
     dims = Dims.from_config(scfg)
@@ -139,17 +141,17 @@ def node_sweep(torch, M, MedusaStep, Dims, cfg, w, dev, seed: int, node_counts, 
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
-    pts = budget.curve(acc, s, counts, step_seconds=timed, dense_s=dense_s)
+    pts = budget.curve(acc, s, counts, step_seconds=timed, dense=dense)
     top = budget.best(pts)
     sparse = {p.nodes: p for p in pts if p.kind == "sparse"}
-    dense = next((p for p in pts if p.kind == "dense"), None)
+    dense256 = next((p for p in pts if p.kind == "dense" and p.nodes == 256), None)
     out = {"tree_s": list(s), "steps_per_point": steps,
            "accuracy": "synthetic per-head rank accuracies 0.8*0.8^k*0.6*0.4^r*U(0.9,1.1), "
                        "heads independent; E[a] is the closed form, not a measured rate",
            "points": [p.as_dict() for p in pts],
            "best": top.as_dict()}
-    if dense is not None and 64 in sparse:
-        out["sparse64_vs_dense"] = sparse[64].tokens_per_s / dense.tokens_per_s
+    if dense256 is not None and 64 in sparse:
+        out["sparse64_vs_dense"] = sparse[64].tokens_per_s / dense256.tokens_per_s
     return out
 
 
@@ -214,6 +216,38 @@ def rope_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, steps: int, warmup:
     ms, n = M.medusa_profile_query("rope")
     return {"base": ROPE_BASE, "steps": steps, "ms_per_step": 1e3 * sec, "steps_per_s": 1.0 / sec,
             "rope_us": 1e3 * ms / n if n else None}
+
+
+def hbm_probe(torch, M, buf, reps: int = 10):
+    """Read ceiling of this GPU: medusa_hbm_read_probe streaming `buf` (the heads' weights)
+    `reps` times, timed with events on the current stream."""
+    sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    nbytes = M.medusa_hbm_probe_bytes(buf.numel() * buf.element_size())
+    M.medusa_hbm_read_probe(buf, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        M.medusa_hbm_read_probe(buf, sink)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) * 1e-3 / reps
+    return {"gbps": nbytes / sec / 1e9, "bytes_per_launch": nbytes, "launches": reps,
+            "avg_us": sec * 1e6}
+
+
+def step_percentiles(torch, step, steps: int):
+    """Per-step durations from events around each step (a pass of its own)."""
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        step.run(bootstrap_root=False, keep_u=False)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([1e3 * a.elapsed_time(b) for a, b in ev])
+    return {"median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90)), "steps": steps}
 
 
 def kernel_source_hash() -> str:
@@ -381,6 +415,9 @@ def main() -> int:
         if n:
             kernels[name] = {"avg_us": 1e3 * ms / n, "launches": n}
 
+    step_us = step_percentiles(torch, step, args.steps)
+    probe = hbm_probe(torch, M, w["w2"])
+    log(f"[bench] probe {probe['gbps']:.0f} GB/s; step median {step_us['median']:.1f} us")
     res = step.results()
     loop = decode_loop_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, args.loop_rounds)
     typical = None
@@ -415,7 +452,7 @@ def main() -> int:
         achieved = ab[DOMINANT] / (hv * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(cfg.name),
-                "kernel": DOMINANT,
+                "kernel": DOMINANT, "frac_of_probe": achieved / probe["gbps"],
                 "bytes_per_launch": ab[DOMINANT], "avg_us": hv, "launches": dom_n}
     out = {
         "metric": METRIC,
@@ -439,6 +476,8 @@ def main() -> int:
         "hbm_gbps": ab["total"] / sec / 1e9,
         "hbm_frac": ab["total"] / sec / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": ab["total"],
+        "step_us": step_us,
+        "hbm_probe": probe,
         "roofline": roof,
         "kernels": kernels,
         "decode_loop": loop,

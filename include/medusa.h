@@ -250,6 +250,16 @@ medusa_status medusa_advance(const medusa_tree_plan* plan, medusa_dtype dt, int 
                              void* k_cache, void* v_cache, int32_t* prefix_lens, void* hidden_out,
                              int32_t* root_out, int32_t* overflow, void* stream);
 
+/* ------------------------------------------------------------------ measurement
+ * HBM read-bandwidth probe (not part of the method): streams the first
+ * medusa_hbm_probe_bytes(bytes) bytes of `buf` (whole 8 KiB blocks) once, with the access
+ * pattern of the heads' GEMV (64 lanes x 16 contiguous bytes per load, non-temporal), and
+ * writes `sink` (a device uint32) only in the rare case its checksum equals one fixed
+ * value.  Timing it with events on `stream` gives the read ceiling that the streaming
+ * kernels are compared with.  buf 16-byte aligned and at least 8 KiB. */
+size_t medusa_hbm_probe_bytes(size_t bytes);
+medusa_status medusa_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------ one-layer verifier
  * A stand-in for the frozen base model that scores the tree (not part of the method):
  * embedding gather, Q/K/V projections, and the attention output projection with the

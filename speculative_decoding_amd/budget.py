@@ -50,20 +50,20 @@ class BudgetPoint:
 
 
 def plans(acc: np.ndarray, tree_s: Sequence[int], node_counts: Iterable[int],
-          dense_s: Optional[Sequence[int]] = None):
-    """(kind, plan) for every sparse budget in node_counts, then the dense tree of dense_s."""
+          dense: Sequence[Sequence[int]] = ()):
+    """(kind, plan) for every sparse budget in node_counts, then the full Cartesian tree of
+    each per-depth branching in `dense`."""
     out = [("sparse", M.medusa_tree_plan_from_accuracy(acc, tree_s, int(n))) for n in node_counts]
-    if dense_s:
-        out.append(("dense", M.medusa_tree_plan_full(dense_s)))
+    out += [("dense", M.medusa_tree_plan_full(ds)) for ds in dense]
     return out
 
 
 def curve(acc: np.ndarray, tree_s: Sequence[int], node_counts: Iterable[int],
           step_seconds: Optional[Callable[[M.TreePlan], float]] = None,
-          dense_s: Optional[Sequence[int]] = None) -> List[BudgetPoint]:
-    """E[a] for each budget (and the dense tree), with t(N) from ``step_seconds`` when given."""
+          dense: Sequence[Sequence[int]] = ()) -> List[BudgetPoint]:
+    """E[a] for each budget (and each dense tree), with t(N) from ``step_seconds`` when given."""
     pts = []
-    for kind, plan in plans(acc, tree_s, node_counts, dense_s):
+    for kind, plan in plans(acc, tree_s, node_counts, dense):
         n, depth, _ = plan.info()
         p = BudgetPoint(kind=kind, nodes=n, max_depth=depth,
                         expected_accept=plan.expected_accept(acc))

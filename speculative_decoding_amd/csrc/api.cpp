@@ -9,6 +9,7 @@
 
 #include "advance.hpp"
 #include "plan_impl.hpp"
+#include "probe.hpp"
 #include "rope.hpp"
 
 using namespace medusa;
@@ -470,6 +471,18 @@ medusa_status medusa_rope(medusa_dtype dt, int M, int Hq, int Hkv, int d, const 
     prof_begin("rope", strm);
     hipError_t e = rope_launch(dt, a, strm);
     prof_end(strm);
+    if (e != hipSuccess) return medusa_internal_hip_error(e);
+    return MEDUSA_OK;
+}
+
+size_t medusa_hbm_probe_bytes(size_t bytes) { return (size_t)hbm_probe_bytes(bytes); }
+
+medusa_status medusa_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return MEDUSA_ERR_NULL;
+    if (hbm_probe_bytes(bytes) < 8192 || !aligned16(buf)) return MEDUSA_ERR_SHAPE;
+    medusa_status st = medusa_internal_device_check();
+    if (st != MEDUSA_OK) return st;
+    hipError_t e = hbm_probe_launch(buf, bytes, sink, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     return MEDUSA_OK;
 }

@@ -1,0 +1,58 @@
+// HBM read-bandwidth probe: the ceiling the streaming kernels are measured against.
+//
+// Every wave streams whole 8 KiB blocks of the buffer with the access pattern of the GEMV
+// kernel (64 lanes x 16 contiguous bytes per instruction, non-temporal), four blocks in
+// flight, and folds them into a checksum that is stored only if it takes one particular
+// value, so the loads stay live without a store per load.
+#include "common.hpp"
+#include "probe.hpp"
+
+namespace medusa {
+
+namespace {
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeBlockBytes = 8192;
+constexpr int kProbeBlocksPerWg = 128;     // 1 MiB per workgroup
+constexpr int kProbeInFlight = 4;
+
+__global__ __launch_bounds__(kProbeThreads) void hbm_probe_kernel(const u32x4* __restrict__ buf,
+                                                                  long long n_blocks,
+                                                                  uint32_t* __restrict__ sink) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    constexpr int kVec = kProbeBlockBytes / 16;             // 16-byte vectors per block
+    const long long first = (long long)blockIdx.x * kProbeBlocksPerWg;
+    uint32_t acc = 0;
+    for (int j = wave * kProbeInFlight; j < kProbeBlocksPerWg; j += 4 * kProbeInFlight) {
+        u32x4 v[kProbeInFlight][kVec / 64];
+#pragma unroll
+        for (int r = 0; r < kProbeInFlight; ++r) {
+            const long long blk = min(first + j + r, n_blocks - 1);
+            const u32x4* p = buf + blk * kVec + lane;
+#pragma unroll
+            for (int c = 0; c < kVec / 64; ++c) v[r][c] = __builtin_nontemporal_load(p + c * 64);
+        }
+#pragma unroll
+        for (int r = 0; r < kProbeInFlight; ++r)
+#pragma unroll
+            for (int c = 0; c < kVec / 64; ++c) acc ^= v[r][c].x ^ v[r][c].w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+}  // namespace
+
+long long hbm_probe_bytes(size_t bytes) {
+    return (long long)(bytes / kProbeBlockBytes) * kProbeBlockBytes;
+}
+
+hipError_t hbm_probe_launch(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    const long long n_blocks = (long long)(bytes / kProbeBlockBytes);
+    const long long grid = (n_blocks + kProbeBlocksPerWg - 1) / kProbeBlocksPerWg;
+    hipLaunchKernelGGL(hbm_probe_kernel, dim3((unsigned)grid), dim3(kProbeThreads), 0, stream,
+                       static_cast<const u32x4*>(buf), n_blocks, sink);
+    return hipGetLastError();
+}
+
+}  // namespace medusa

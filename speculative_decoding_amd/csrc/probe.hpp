@@ -1,0 +1,14 @@
+// HBM read-bandwidth probe (probe.hip): declarations shared with the C API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace medusa {
+
+// Bytes one probe launch reads from a buffer of `bytes` (whole 8 KiB blocks).
+long long hbm_probe_bytes(size_t bytes);
+hipError_t hbm_probe_launch(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+}  // namespace medusa

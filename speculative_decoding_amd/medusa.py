@@ -294,6 +294,17 @@ def medusa_rope(dt, M, Hq, Hkv, d, positions, base, q, k, stream=None):
     _check("medusa_rope", st)
 
 
+def medusa_hbm_probe_bytes(nbytes: int) -> int:
+    return int(lib().medusa_hbm_probe_bytes(int(nbytes)))
+
+
+def medusa_hbm_read_probe(buf, sink, stream=None):
+    """One streaming read of a device tensor's bytes; sink: a device tensor of >= 4 bytes."""
+    st = lib().medusa_hbm_read_probe(_ptr(buf, None, "buf"), buf.numel() * buf.element_size(),
+                                     _ptr(sink, None, "sink"), _stream(stream))
+    _check("medusa_hbm_read_probe", st)
+
+
 def medusa_proxy_workspace(dt, M, H, Hq, Hkv, d) -> int:
     return int(lib().medusa_proxy_workspace(_dt(dt), M, H, Hq, Hkv, d))
 

@@ -206,3 +206,14 @@ def test_rope_error_paths():
         assert L.medusa_rope(1, M, Hq, Hkv, d, 16, base, 16, 16, None) == 2, (M, Hq, Hkv, d, base)
     # misaligned q for bf16 (8-byte quads)
     assert L.medusa_rope(1, 4, 2, 1, 64, 16, 1e4, 20, 16, None) == 2
+
+
+def test_probe_error_paths():
+    L = lib()
+    from speculative_decoding_amd import medusa as M
+    assert M.medusa_hbm_probe_bytes(8192 * 3 + 100) == 8192 * 3
+    assert M.medusa_hbm_probe_bytes(8191) == 0
+    assert L.medusa_hbm_read_probe(None, 1 << 20, 16, None) == 1
+    assert L.medusa_hbm_read_probe(16, 1 << 20, None, None) == 1
+    assert L.medusa_hbm_read_probe(16, 4096, 16, None) == 2          # under one block
+    assert L.medusa_hbm_read_probe(24, 1 << 20, 16, None) == 2       # misaligned

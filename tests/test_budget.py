@@ -105,7 +105,7 @@ def test_sparse_choice_maximises_expected_accept(widths, seed):
 
 def test_root_only_and_monotone():
     acc = _acc(6, (10, 5, 4, 4))
-    pts = budget.curve(acc, (10, 5, 4, 4), [1, 2, 16, 64, 256, 341, 1024], dense_s=(3, 4, 4, 4))
+    pts = budget.curve(acc, (10, 5, 4, 4), [1, 2, 16, 64, 256, 341, 1024], dense=[(3, 4, 4, 4)])
     sparse = [p for p in pts if p.kind == "sparse"]
     assert sparse[0].nodes == 1 and sparse[0].expected_accept == 0.0 and sparse[0].max_depth == 0
     e = [p.expected_accept for p in sparse]
