@@ -40,6 +40,24 @@ __global__ __launch_bounds__(256) void build_tree_kernel(DevicePlan plan, int K,
 
 constexpr int kAcceptThreads = 1024;
 constexpr int kMaxNodes = MEDUSA_MAX_NODES;
+constexpr int kMergeBatch = 16;     // tile partials per lane in flight at once
+
+// Fold tiles t0, t0 + stride, ... (kMergeBatch of them, those below n) of one node's
+// argmax partials into (bv, bi): every load is issued before the first comparison.
+__device__ __forceinline__ void merge_batch(const float* pv, const int32_t* pi, int t0, int n,
+                                            int stride, float& bv, int& bi) {
+    float v[kMergeBatch];
+    int id[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+        const int t = min(t0 + j * stride, n - 1);
+        v[j] = pv[t];
+        id[j] = pi[t];
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+        if (t0 + j * stride < n && better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
+}
 
 // The kept branch: the deepest accepted node, the lowest index among equals (atomicMax on
 // (depth, -index)); its path root-first, the candidates on it, then the node's argmax.
@@ -83,8 +101,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const int b = blockIdx.x;
     const int N = plan.n_nodes;
     const int D = plan.max_depth;
-    // 16 lanes per node: each lane scans a strided share of the node's tile partials with
-    // eight loads in flight, then the 16 lanes reduce.
+    // 16 lanes per node: each lane scans a strided share of the node's tile partials,
+    // kMergeBatch loads in flight at a time, then the 16 lanes reduce.
     constexpr int kPerNode = 16;
     for (int i0 = 0; i0 < N; i0 += kAcceptThreads / kPerNode) {
         const int i = i0 + threadIdx.x / kPerNode;
@@ -94,19 +112,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
         if (i < N) {
             const float* pv = part_val + ((long long)b * N + i) * n_tiles;
             const int32_t* pi = part_idx + ((long long)b * N + i) * n_tiles;
-            for (int t0 = sub; t0 < n_tiles; t0 += 8 * kPerNode) {
-                float v[8];
-                int id[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int t = t0 + j * kPerNode;
-                    v[j] = t < n_tiles ? pv[t] : -INFINITY;
-                    id[j] = t < n_tiles ? pi[t] : INT_MAX;
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
-            }
+            for (int t0 = sub; t0 < n_tiles; t0 += kMergeBatch * kPerNode)
+                merge_batch(pv, pi, t0, n_tiles, kPerNode, bv, bi);
         }
         row_best(bv, bi);     // the 16 lanes of a node form one DPP row
         if (sub == 0 && i < N) {
@@ -153,29 +160,30 @@ __global__ __launch_bounds__(kAcceptThreads) void typical_accept_kernel(DevicePl
         const long long base = ((long long)b * N + min(i, N - 1)) * nt;
         float bv = -INFINITY;
         int bi = INT_MAX;
-        for (int t0 = sub; t0 < nt; t0 += 8 * kPerNode) {
-            float v[8];
-            int id[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = t0 + j * kPerNode;
-                v[j] = t < nt ? a.part_val[base + t] : -INFINITY;
-                id[j] = t < nt ? a.part_idx[base + t] : INT_MAX;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
-        }
+        for (int t0 = sub; t0 < nt; t0 += kMergeBatch * kPerNode)
+            merge_batch(a.part_val + base, a.part_idx + base, t0, nt, kPerNode, bv, bi);
         row_best(bv, bi);       // every lane of the node's row: the maximum and its id
         // the tiles' sums rescaled to the node's maximum: with y = (tile max - max) / T,
-        // Z = sum z e^y and S = sum e^y (s + z y), so that H = ln Z - S / Z
+        // Z = sum z e^y and S = sum e^y (s + z y), so that H = ln Z - S / Z; the loads of
+        // a batch are all issued before the first is used
         float z = 0.f, sx = 0.f;
-        for (int t = sub; t < nt; t += kPerNode) {
-            const float y = (a.part_val[base + t] - bv) * a.inv_t;
-            const float g = __builtin_amdgcn_exp2f(y * kLog2e);
-            const float zt = a.part_z[base + t];
-            z += g * zt;
-            sx += g * (a.part_s[base + t] + zt * y);
+        for (int t0 = sub; t0 < nt; t0 += kMergeBatch * kPerNode) {
+            float pv[kMergeBatch], pz[kMergeBatch], ps[kMergeBatch];
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                const int t = min(t0 + j * kPerNode, nt - 1);
+                pv[j] = a.part_val[base + t];
+                pz[j] = a.part_z[base + t];
+                ps[j] = a.part_s[base + t];
+            }
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                if (t0 + j * kPerNode >= nt) continue;
+                const float y = (pv[j] - bv) * a.inv_t;
+                const float g = __builtin_amdgcn_exp2f(y * kLog2e);
+                z += g * pz[j];
+                sx += g * (ps[j] + pz[j] * y);
+            }
         }
         z = row_sum16(z);
         sx = row_sum16(sx);
