@@ -114,6 +114,7 @@ class MedusaStep:
     # ---- the four calls plus the verifier layer, in step order
     def heads(self, bootstrap_root: bool = False, keep_u: bool = True):
         d, w = self.dims, self.w
+        self.u_written = keep_u
         M.medusa_heads_forward(d.dtype, d.B, d.H, d.V, d.K, w["h"], w["w1"], w["b1"], w["w2"],
                                w["w_lm"] if bootstrap_root else None, d.s, d.s_max, self.topk_ids,
                                self.topk_vals, self.root_ids if bootstrap_root else None,
@@ -224,4 +225,6 @@ class MedusaStep:
                  "k_tree", "v_tree", "o", "node_hidden", "node_argmax", "accept_len",
                  "accept_nodes", "accept_tokens", "head_logits", "verify_logits", "node_prob",
                  "node_tau"]
-        return {n: host(getattr(self, n)) for n in names}
+        out = {n: host(getattr(self, n)) for n in names if n != "u"}
+        out["u"] = host(self.u) if getattr(self, "u_written", False) else None
+        return out

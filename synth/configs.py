@@ -142,6 +142,14 @@ CONFIGS = {
         tree_s=(10, 5, 4, 3), n_nodes=341, Hq=8, Hkv=2, d=128, L=300, Lcap=320,
         sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
         sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
+    # the library's limits at a small shape: 8 heads, top-64 on the first, a 1024-node
+    # tree (several mask words, 2048 verified rows), an empty and a ragged prefix
+    "small_max": Config(
+        name="small_max", B=2, H=512, V=3001, K=8, s=(64, 4, 3, 2, 2, 2, 2, 2), tree="sparse",
+        tree_s=(64, 4, 3, 2, 2, 2, 2, 2), n_nodes=1024, Hq=4, Hkv=1, d=64, lens=(0, 201),
+        Lcap=256,
+        sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
+        sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
     # the verifier with rotary positions (base 10000): ragged prefixes including an empty
     # one, and a loop case whose rounds move the positions on
     "small_rope": Config(

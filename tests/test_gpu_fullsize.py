@@ -12,7 +12,9 @@ from tests.gpu_util import PLANTS, compare_step, oracle_plan, planted, run_gpu, 
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-CASES = [("8b", 0), ("8b", 1), ("mid", 0), ("dense", 0), ("batched70b", 0)]
+# seeds with a stored plant: 8B and Mid 0-4, Dense and Batched 70B 0-2
+CASES = ([("8b", s) for s in range(5)] + [("mid", s) for s in range(5)] +
+         [("dense", s) for s in range(3)] + [("batched70b", s) for s in range(3)])
 
 
 @pytest.fixture(scope="module")

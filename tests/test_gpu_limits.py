@@ -1,0 +1,40 @@
+"""GPU parity at the library's limits, at a small shape: eight heads (the most allowed),
+top-64 on the first (the largest top-k), and a 1024-node tree (the largest plan: depth 8,
+sixteen mask words, 2048 verified rows over two sequences) with an empty and a ragged
+prefix.  The inputs are not planted (no planting opens a margin at 2048 nodes), so each
+node's argmax may take either side of a near-tie and the accept results must follow from
+the device's own decisions; the heads' top-65 gaps are checked to be far above the fp32
+rounding of the device's logits, so their top-k is exact."""
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_inputs
+from tests.gpu_util import compare_step, oracle_plan, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from speculative_decoding_amd import lib
+    lib()
+    return torch.device("cuda:0")
+
+
+def test_limits_step(dev):
+    say("[limits: K=8, top-64, 1024 nodes, B=2]")
+    inp = make_inputs("small_max", 0)
+    cfg = inp.cfg
+    plan = oracle_plan(inp)
+    assert plan.n_nodes == 1024 and plan.max_depth == 8 and plan.mask_words == 16
+    ref = oracle.step(inp, plan)
+    for b in range(cfg.B):
+        for k in range(cfg.K):
+            v = np.sort(ref.head_logits[b, k])[::-1][: cfg.s[k] + 1]
+            assert np.min(v[:-1] - v[1:]) >= 1e-4, "the draw has a near-tie in a head's top-k"
+    _, got = run_gpu(inp, dev, keep_logits=False, keep_u=False)
+    compare_step(inp, got, ref, plan=plan, check_logits=False, check_u=False)
+    say(f"    accept {got['accept_len'].tolist()}")
