@@ -59,7 +59,9 @@ HeadsLayout heads_layout(medusa_dtype dt, int B, int H, int V, int K, int s_max,
 }
 
 struct VerifyLayout {
-    size_t part_val = 0, part_idx = 0, part_z = 0, part_s = 0, cand_logit = 0, total = 0;
+    size_t part_val = 0, part_idx = 0, node_arg = 0;
+    size_t part_z = 0, part_s = 0, cand_logit = 0, node_max = 0, node_z = 0, node_tau = 0;
+    size_t total = 0;
     int n_tiles = 0;
 };
 
@@ -72,10 +74,14 @@ VerifyLayout verify_layout(medusa_dtype dt, int M, int V, int H, bool typical = 
     L.n_tiles = n_tiles_for(dt, M, EPI_ARGMAX, V, H);
     L.part_val = c.take((size_t)M * L.n_tiles * sizeof(float));
     L.part_idx = c.take((size_t)M * L.n_tiles * sizeof(int32_t));
+    L.node_arg = c.take((size_t)M * sizeof(int32_t));        // when the caller wants none
     if (typical) {
         L.part_z = c.take((size_t)M * L.n_tiles * sizeof(float));
         L.part_s = c.take((size_t)M * L.n_tiles * sizeof(float));
         L.cand_logit = c.take((size_t)M * sizeof(float));
+        L.node_max = c.take((size_t)M * sizeof(float));
+        L.node_z = c.take((size_t)M * sizeof(float));
+        L.node_tau = c.take((size_t)M * sizeof(float));
     }
     L.total = c.off;
     return L;
@@ -354,8 +360,9 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
     hipError_t e = timed_gemm("verify_lmhead", dt, EPI_ARGMAX, g, strm);
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     prof_begin("verify_accept", strm);
+    int32_t* arg = node_argmax ? node_argmax : reinterpret_cast<int32_t*>(wsb + L.node_arg);
     e = accept_launch(medusa_internal_device_plan(plan), B, L.n_tiles, pv, pi, node_tokens,
-                      node_argmax, accept_len, accept_nodes, accept_tokens, strm);
+                      arg, accept_len, accept_nodes, accept_tokens, strm);
     prof_end(strm);
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     return MEDUSA_OK;
@@ -432,9 +439,11 @@ medusa_status medusa_verify_accept_typical(const medusa_tree_plan* plan, medusa_
     ta.inv_t = g.typ.inv_t;
     ta.epsilon = epsilon;
     ta.delta = delta;
-    ta.node_argmax = node_argmax;
+    ta.node_argmax = node_argmax ? node_argmax : reinterpret_cast<int32_t*>(wsb + L.node_arg);
+    ta.node_max = reinterpret_cast<float*>(wsb + L.node_max);
+    ta.node_z = reinterpret_cast<float*>(wsb + L.node_z);
+    ta.node_tau = node_tau ? node_tau : reinterpret_cast<float*>(wsb + L.node_tau);
     ta.node_prob = node_prob;
-    ta.node_tau = node_tau;
     ta.accept_len = accept_len;
     ta.accept_nodes = accept_nodes;
     ta.accept_tokens = accept_tokens;

@@ -124,6 +124,8 @@ hipError_t build_tree_launch(const DevicePlan& plan, int B, int K, int s_max,
                              const int32_t* root_ids, const int32_t* topk_ids,
                              const int32_t* prefix_lens, int32_t* node_tokens,
                              int32_t* position_ids, hipStream_t stream);
+// Greedy acceptance from the EPI_ARGMAX partials: a per-node merge over many workgroups
+// (node_argmax [B, n_nodes], required), then the level walk, one workgroup per sequence.
 hipError_t accept_launch(const DevicePlan& plan, int B, int n_tiles, const float* part_val,
                          const int32_t* part_idx, const int32_t* node_tokens,
                          int32_t* node_argmax, int32_t* accept_len, int32_t* accept_nodes,
@@ -140,9 +142,11 @@ struct TypicalAccept {
     const float* cand_logit;
     const int32_t* node_tokens;
     float inv_t, epsilon, delta;
-    int32_t* node_argmax;        // may be null
+    int32_t* node_argmax;        // [B, n_nodes], required
+    float* node_max;             // [B, n_nodes] scratch
+    float* node_z;               // [B, n_nodes] scratch
+    float* node_tau;             // [B, n_nodes], required
     float* node_prob;            // may be null
-    float* node_tau;             // may be null
     int32_t* accept_len;
     int32_t* accept_nodes;
     int32_t* accept_tokens;

@@ -40,7 +40,22 @@ __global__ __launch_bounds__(256) void build_tree_kernel(DevicePlan plan, int K,
 
 constexpr int kAcceptThreads = 1024;
 constexpr int kMaxNodes = MEDUSA_MAX_NODES;
+constexpr int kMergeThreads = 256;  // node merge: four nodes (one per wave) per workgroup
 constexpr int kMergeBatch = 16;     // tile partials per lane in flight at once
+
+struct NodeMerge {
+    int n_rows;                 // B * n_nodes
+    int n_tiles;
+    const float* part_val;
+    const int32_t* part_idx;
+    const float* part_z;        // null: argmax only (greedy acceptance)
+    const float* part_s;
+    float inv_t, epsilon, delta;
+    int32_t* node_argmax;       // [n_rows]
+    float* node_max;            // [n_rows], typical only
+    float* node_z;
+    float* node_tau;
+};
 
 // Fold tiles t0, t0 + stride, ... (kMergeBatch of them, those below n) of one node's
 // argmax partials into (bv, bi): every load is issued before the first comparison.
@@ -88,12 +103,61 @@ __device__ __forceinline__ void emit_branch(const DevicePlan& plan, int b,
     }
 }
 
-// One workgroup per sequence: merge the lm_head argmax partials of every node, then walk
-// the tree level by level.
-__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
-    DevicePlan plan, int n_tiles, const float* __restrict__ part_val,
-    const int32_t* __restrict__ part_idx, const int32_t* __restrict__ node_tokens,
-    int32_t* __restrict__ node_argmax, int32_t* __restrict__ accept_len,
+// Per-node merge of the lm_head tile partials, one wave per node over many workgroups so
+// the partials stream through many CUs: the node's argmax and, for typical acceptance,
+// its maximum, softmax normaliser and threshold.  With y = (tile max - node max) / T, the
+// tiles' sums combine as Z = sum z e^y and S = sum e^y (s + z y), and H = ln Z - S / Z.
+__global__ __launch_bounds__(kMergeThreads) void node_merge_kernel(NodeMerge a) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const int row = blockIdx.x * (kMergeThreads / kWave) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= a.n_rows) return;            // a whole wave: this kernel has no block barrier
+    const int nt = a.n_tiles;
+    const long long base = (long long)row * nt;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int t0 = lane; t0 < nt; t0 += kMergeBatch * kWave)
+        merge_batch(a.part_val + base, a.part_idx + base, t0, nt, kWave, bv, bi);
+    wave_best(bv, bi);
+    if (!a.part_z) {
+        if (lane == 0) a.node_argmax[row] = bi;
+        return;
+    }
+    float z = 0.f, sx = 0.f;
+    for (int t0 = lane; t0 < nt; t0 += kMergeBatch * kWave) {
+        float pv[kMergeBatch], pz[kMergeBatch], ps[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {     // every load before the first use
+            const int t = min(t0 + j * kWave, nt - 1);
+            pv[j] = a.part_val[base + t];
+            pz[j] = a.part_z[base + t];
+            ps[j] = a.part_s[base + t];
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            if (t0 + j * kWave >= nt) continue;
+            const float y = (pv[j] - bv) * a.inv_t;
+            const float g = __builtin_amdgcn_exp2f(y * kLog2e);
+            z += g * pz[j];
+            sx += g * (ps[j] + pz[j] * y);
+        }
+    }
+    z = wave_sum_dpp(z);
+    sx = wave_sum_dpp(sx);
+    if (lane == 0) {
+        const float H = logf(z) - sx / z;
+        a.node_argmax[row] = bi;
+        a.node_max[row] = bv;
+        a.node_z[row] = z;
+        a.node_tau[row] = fminf(a.epsilon, a.delta * expf(-H));
+    }
+}
+
+// Greedy walk, one workgroup per sequence: a node is accepted when its parent is and its
+// token is the parent's argmax.
+__global__ __launch_bounds__(kAcceptThreads) void accept_walk_kernel(
+    DevicePlan plan, const int32_t* __restrict__ node_argmax,
+    const int32_t* __restrict__ node_tokens, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ accept_nodes, int32_t* __restrict__ accept_tokens) {
     __shared__ int s_arg[kMaxNodes];
     __shared__ unsigned char s_acc[kMaxNodes];
@@ -101,27 +165,10 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const int b = blockIdx.x;
     const int N = plan.n_nodes;
     const int D = plan.max_depth;
-    // 16 lanes per node: each lane scans a strided share of the node's tile partials,
-    // kMergeBatch loads in flight at a time, then the 16 lanes reduce.
-    constexpr int kPerNode = 16;
-    for (int i0 = 0; i0 < N; i0 += kAcceptThreads / kPerNode) {
-        const int i = i0 + threadIdx.x / kPerNode;
-        const int sub = threadIdx.x % kPerNode;
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-        if (i < N) {
-            const float* pv = part_val + ((long long)b * N + i) * n_tiles;
-            const int32_t* pi = part_idx + ((long long)b * N + i) * n_tiles;
-            for (int t0 = sub; t0 < n_tiles; t0 += kMergeBatch * kPerNode)
-                merge_batch(pv, pi, t0, n_tiles, kPerNode, bv, bi);
-        }
-        row_best(bv, bi);     // the 16 lanes of a node form one DPP row
-        if (sub == 0 && i < N) {
-            s_arg[i] = bi;
-            if (node_argmax) node_argmax[(long long)b * N + i] = bi;
-        }
+    for (int i = threadIdx.x; i < N; i += kAcceptThreads) {
+        s_arg[i] = node_argmax[(long long)b * N + i];
+        s_acc[i] = i == 0;
     }
-    for (int i = threadIdx.x; i < N; i += kAcceptThreads) s_acc[i] = i == 0;
     if (threadIdx.x == 0) s_best = 0;
     __syncthreads();
     const int32_t* tok = node_tokens + (long long)b * N;
@@ -136,81 +183,35 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     emit_branch(plan, b, s_acc, s_arg, tok, s_best, accept_len, accept_nodes, accept_tokens);
 }
 
-// Per node: argmax, the softmax normaliser and the entropy merged over the lm_head tiles,
-// and the threshold; per candidate: its probability under the parent's distribution; then
-// the level walk.  One workgroup per sequence, 16 lanes per node for the merges.
-__global__ __launch_bounds__(kAcceptThreads) void typical_accept_kernel(DevicePlan plan,
-                                                                        TypicalAccept a) {
+// Typical walk, one workgroup per sequence: each candidate's probability under its
+// parent's distribution, p = e^((logit - max) / T) / Z, and a node is accepted when its
+// parent is and p exceeds the parent's threshold.
+__global__ __launch_bounds__(kAcceptThreads) void typical_walk_kernel(DevicePlan plan,
+                                                                      TypicalAccept a) {
     __shared__ int s_arg[kMaxNodes];
-    __shared__ float s_max[kMaxNodes];
-    __shared__ float s_z[kMaxNodes];
     __shared__ float s_tau[kMaxNodes];
     __shared__ float s_prob[kMaxNodes];
     __shared__ unsigned char s_acc[kMaxNodes];
     __shared__ int s_best;
     constexpr float kLog2e = 1.4426950408889634f;
-    constexpr int kPerNode = 16;
     const int b = blockIdx.x;
     const int N = plan.n_nodes;
     const int D = plan.max_depth;
-    const int nt = a.n_tiles;
-    for (int i0 = 0; i0 < N; i0 += kAcceptThreads / kPerNode) {
-        const int i = i0 + threadIdx.x / kPerNode;
-        const int sub = threadIdx.x % kPerNode;
-        const long long base = ((long long)b * N + min(i, N - 1)) * nt;
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-        for (int t0 = sub; t0 < nt; t0 += kMergeBatch * kPerNode)
-            merge_batch(a.part_val + base, a.part_idx + base, t0, nt, kPerNode, bv, bi);
-        row_best(bv, bi);       // every lane of the node's row: the maximum and its id
-        // the tiles' sums rescaled to the node's maximum: with y = (tile max - max) / T,
-        // Z = sum z e^y and S = sum e^y (s + z y), so that H = ln Z - S / Z; the loads of
-        // a batch are all issued before the first is used
-        float z = 0.f, sx = 0.f;
-        for (int t0 = sub; t0 < nt; t0 += kMergeBatch * kPerNode) {
-            float pv[kMergeBatch], pz[kMergeBatch], ps[kMergeBatch];
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {
-                const int t = min(t0 + j * kPerNode, nt - 1);
-                pv[j] = a.part_val[base + t];
-                pz[j] = a.part_z[base + t];
-                ps[j] = a.part_s[base + t];
-            }
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {
-                if (t0 + j * kPerNode >= nt) continue;
-                const float y = (pv[j] - bv) * a.inv_t;
-                const float g = __builtin_amdgcn_exp2f(y * kLog2e);
-                z += g * pz[j];
-                sx += g * (ps[j] + pz[j] * y);
-            }
-        }
-        z = row_sum16(z);
-        sx = row_sum16(sx);
-        if (sub == 0 && i < N) {
-            const float H = logf(z) - sx / z;
-            const float tau = fminf(a.epsilon, a.delta * expf(-H));
-            s_arg[i] = bi;
-            s_max[i] = bv;
-            s_z[i] = z;
-            s_tau[i] = tau;
-            if (a.node_argmax) a.node_argmax[(long long)b * N + i] = bi;
-            if (a.node_tau) a.node_tau[(long long)b * N + i] = tau;
-        }
-    }
-    if (threadIdx.x == 0) s_best = 0;
-    __syncthreads();
+    const long long o = (long long)b * N;
     for (int c = threadIdx.x; c < N; c += kAcceptThreads) {
+        s_arg[c] = a.node_argmax[o + c];
+        s_tau[c] = a.node_tau[o + c];
         float p = 1.f;
         if (c > 0) {
             const int par = plan.parent[c];
-            const float y = (a.cand_logit[(long long)b * N + c] - s_max[par]) * a.inv_t;
-            p = __builtin_amdgcn_exp2f(y * kLog2e) / s_z[par];
+            const float y = (a.cand_logit[o + c] - a.node_max[o + par]) * a.inv_t;
+            p = __builtin_amdgcn_exp2f(y * kLog2e) / a.node_z[o + par];
         }
         s_prob[c] = p;
         s_acc[c] = c == 0;
-        if (a.node_prob) a.node_prob[(long long)b * N + c] = p;
+        if (a.node_prob) a.node_prob[o + c] = p;
     }
+    if (threadIdx.x == 0) s_best = 0;
     __syncthreads();
     for (int d = 1; d <= D; ++d) {
         for (int i = threadIdx.x; i < N; i += kAcceptThreads) {
@@ -220,8 +221,8 @@ __global__ __launch_bounds__(kAcceptThreads) void typical_accept_kernel(DevicePl
         }
         __syncthreads();
     }
-    emit_branch(plan, b, s_acc, s_arg, a.node_tokens + (long long)b * N, s_best, a.accept_len,
-                a.accept_nodes, a.accept_tokens);
+    emit_branch(plan, b, s_acc, s_arg, a.node_tokens + o, s_best, a.accept_len, a.accept_nodes,
+                a.accept_tokens);
 }
 
 // Next round (same section: the longest accepted branch is kept and its last hidden state
@@ -268,7 +269,26 @@ __global__ __launch_bounds__(256) void advance_kernel(AdvanceArgs a) {
 
 hipError_t typical_accept_launch(const DevicePlan& plan, int B, const TypicalAccept& a,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(typical_accept_kernel, dim3(B), dim3(kAcceptThreads), 0, stream, plan, a);
+    NodeMerge m{};
+    m.n_rows = B * plan.n_nodes;
+    m.n_tiles = a.n_tiles;
+    m.part_val = a.part_val;
+    m.part_idx = a.part_idx;
+    m.part_z = a.part_z;
+    m.part_s = a.part_s;
+    m.inv_t = a.inv_t;
+    m.epsilon = a.epsilon;
+    m.delta = a.delta;
+    m.node_argmax = a.node_argmax;
+    m.node_max = a.node_max;
+    m.node_z = a.node_z;
+    m.node_tau = a.node_tau;
+    const int per = kMergeThreads / kWave;
+    hipLaunchKernelGGL(node_merge_kernel, dim3((m.n_rows + per - 1) / per), dim3(kMergeThreads), 0,
+                       stream, m);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(typical_walk_kernel, dim3(B), dim3(kAcceptThreads), 0, stream, plan, a);
     return hipGetLastError();
 }
 
@@ -292,9 +312,19 @@ hipError_t accept_launch(const DevicePlan& plan, int B, int n_tiles, const float
                          const int32_t* part_idx, const int32_t* node_tokens,
                          int32_t* node_argmax, int32_t* accept_len, int32_t* accept_nodes,
                          int32_t* accept_tokens, hipStream_t stream) {
-    hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(kAcceptThreads), 0, stream, plan, n_tiles,
-                       part_val, part_idx, node_tokens, node_argmax, accept_len, accept_nodes,
-                       accept_tokens);
+    NodeMerge m{};
+    m.n_rows = B * plan.n_nodes;
+    m.n_tiles = n_tiles;
+    m.part_val = part_val;
+    m.part_idx = part_idx;
+    m.node_argmax = node_argmax;
+    const int per = kMergeThreads / kWave;
+    hipLaunchKernelGGL(node_merge_kernel, dim3((m.n_rows + per - 1) / per), dim3(kMergeThreads), 0,
+                       stream, m);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(accept_walk_kernel, dim3(B), dim3(kAcceptThreads), 0, stream, plan,
+                       node_argmax, node_tokens, accept_len, accept_nodes, accept_tokens);
     return hipGetLastError();
 }
 
