@@ -594,11 +594,13 @@ __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmB
     constexpr int NI = ROWS / RPI;            // 16-byte loads per lane per chunk
     constexpr int VPR = CH / 8;               // 16-byte vectors per X row chunk
     constexpr int XV = (MT * 16 * VPR + NTH - 1) / NTH;   // ... per thread
-    // X rows past the tile land in a spare slot at the end (every thread stores)
-    __shared__ __align__(16) bf16_t xs[MT * 16 * XP + 8];
-    __shared__ __align__(16) bf16_t wt[NWV][ROWS * XP];
-    __shared__ float red_v[NWV][MT * 16];
-    __shared__ int red_i[NWV][MT * 16];
+    // X rows past the tile land in a spare slot at the end (every thread stores); the
+    // layout is rowstream_lds()'s
+    extern __shared__ __align__(16) unsigned char rs_lds[];
+    bf16_t* xs = reinterpret_cast<bf16_t*>(rs_lds);                          // [MT*16*XP + 8]
+    auto& wt = *reinterpret_cast<bf16_t (*)[NWV][ROWS * XP]>(xs + MT * 16 * XP + 8);
+    auto& red_v = *reinterpret_cast<float (*)[NWV][MT * 16]>(&wt[NWV][0]);
+    auto& red_i = *reinterpret_cast<int (*)[NWV][MT * 16]>(&red_v[NWV][0]);
 
     const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
     const int nblocks = bt.total_tiles * n_mb;
@@ -711,7 +713,8 @@ __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmB
         }
     }
     // the top-s epilogue needs Mb * NWG floats of scratch: the W tiles are free by now
-    static_assert(EPI != EPI_TOPS || sizeof(wt) >= 16 * NWG * sizeof(float), "top-s scratch");
+    static_assert(EPI != EPI_TOPS || sizeof(bf16_t) * NWV * ROWS * XP >= 16 * NWG * sizeof(float),
+                  "top-s scratch");
     __syncthreads();
     tile_epilogue<MT, RT, NWG, EPI, NWV>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane,
                                          reinterpret_cast<unsigned char*>(&wt[0][0]), red_v, red_i);
@@ -1054,190 +1057,6 @@ __global__ __launch_bounds__(NW * kWave) void gemm_cu_partial_kernel(const GemmB
                 if (m < bt.M) part[(long long)m * N + n] = acc[rt][mt][r];
             }
     }
-}
-
-// lm_head over the tree nodes (argmax epilogue), one workgroup per CU.  NW waves of 16*RT
-// weight rows each stream the full contraction through a register ring of PF chunks and a
-// wave-private LDS transpose.  The (up to 64) input rows are staged in LDS one slab of
-// 512 columns at a time, with the next slab held in registers meanwhile.  So the
-// workgroup synchronises twice per eight 64-column chunks instead of twice per chunk, and
-// every CU reads the input rows once instead of once per workgroup.
-constexpr int kSlab = 512;
-
-size_t slab_argmax_lds(int nw, int rt) {
-    return (size_t)64 * (kSlab + 8) * 2 + (size_t)nw * 16 * rt * (64 + 8) * 2 + (size_t)nw * 64 * 8;
-}
-
-template <int NW, int RT, int PF, int EPI>
-__global__ __launch_bounds__(NW * kWave) void gemm_slab_argmax_kernel(const GemmBatch bt) {
-    constexpr int MT = 4;
-    constexpr int CH = 64;
-    constexpr int ROWS = 16 * RT;
-    constexpr int NWG = NW * ROWS;
-    constexpr int XP = CH + 8;
-    constexpr int LPR = CH / 8;
-    constexpr int RPI = kWave / LPR;
-    constexpr int NI = ROWS / RPI;
-    constexpr int KS = CH / 32;
-    constexpr int SP = kSlab + 8;
-    constexpr int NT = NW * kWave;
-    constexpr int SV = MT * 16 * (kSlab / 8) / NT;     // slab vectors per thread
-    constexpr int CPS = kSlab / CH;                    // chunks per slab
-    static_assert(SV * NT == MT * 16 * (kSlab / 8), "slab split over the threads");
-    static_assert(CPS % PF == 0, "ring slots repeat within a slab");
-    extern __shared__ __align__(16) unsigned char dyn_slab[];
-    bf16_t* xs = reinterpret_cast<bf16_t*>(dyn_slab);                       // [64][SP]
-    bf16_t* wt = xs + MT * 16 * SP;                                         // [NW][ROWS*XP]
-    auto& red_v = *reinterpret_cast<float (*)[NW][MT * 16]>(wt + NW * ROWS * XP);
-    auto& red_i = *reinterpret_cast<int (*)[NW][MT * 16]>(&red_v[NW][0]);
-
-    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
-    const int nblocks = bt.total_tiles * n_mb;
-    const int bid = xcd_logical_block(blockIdx.x, nblocks);
-    const int mb = bid % n_mb;
-    const int t = bid / n_mb;
-    const GemmProblem& P = bt.p[problem_of(bt, t)];
-    const int tile = t - P.tile_begin;
-    const int K = bt.K;
-    const int N = P.N;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int ln = lane & 15;
-    const int lg = lane >> 4;
-    const int n_wave = tile * NWG + wave * ROWS;
-    const int m0 = mb * MT * 16;
-    const int Mb = min(bt.M - m0, MT * 16);
-    const int n_ch = K / CH;
-    const int n_slabs = K / kSlab;
-
-    // input slab vectors of this thread: rows without a source read row 0, zeroed on store
-    const bf16_t* X = static_cast<const bf16_t*>(P.X);
-    const bf16_t* xsrc[SV];
-    bool xok[SV];
-    int xdst[SV];
-#pragma unroll
-    for (int j = 0; j < SV; ++j) {
-        const int idx = threadIdx.x + j * NT;
-        const int m = idx / (kSlab / 8);
-        const int c = idx - m * (kSlab / 8);
-        long long r = 0;
-        bool ok = m < Mb;
-        if (ok) {
-            r = m0 + m;
-            if (P.x_rows) {
-                r = P.x_rows[m0 + m];
-                ok = r >= 0 && r < bt.x_rows_bound;
-                if (!ok) r = 0;
-            }
-        }
-        xok[j] = ok;
-        xsrc[j] = X + r * P.x_stride + c * 8;
-        xdst[j] = m * SP + c * 8;
-    }
-    u32x4 xv[SV];
-    auto slab_load = [&](int sl) {
-        const int ks = min(sl, n_slabs - 1) * kSlab;
-#pragma unroll
-        for (int j = 0; j < SV; ++j) xv[j] = *reinterpret_cast<const u32x4*>(xsrc[j] + ks);
-    };
-    auto slab_store = [&]() {
-#pragma unroll
-        for (int j = 0; j < SV; ++j)
-            *reinterpret_cast<u32x4*>(xs + xdst[j]) = xok[j] ? xv[j] : u32x4{0u, 0u, 0u, 0u};
-    };
-
-    const bf16_t* W = static_cast<const bf16_t*>(P.W);
-    const int half = lane / LPR;
-    const int col = (lane % LPR) * 8;
-    const u32x4* wsrc[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int n = min(n_wave + RPI * i + half, N - 1);
-        wsrc[i] = reinterpret_cast<const u32x4*>(W + (long long)n * K + col);
-    }
-    u32x4 wr[PF][NI];
-    auto load_w = [&](int q, int c) {
-        const int kc = min(c, n_ch - 1) * CH;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) wr[q][i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
-    };
-    bf16_t* wtile = wt + wave * ROWS * XP;
-
-    floatx4 acc[RT][MT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int q = 0; q < PF; ++q) load_w(q, q);
-    slab_load(0);
-    slab_store();
-    slab_load(1);
-    __syncthreads();
-    for (int c0 = 0; c0 < n_ch; c0 += CPS) {
-        if (c0 > 0) {
-            // every wave is done with the previous slab: replace it with the prefetched one
-            __syncthreads();
-            slab_store();
-            __syncthreads();
-            slab_load(c0 / CPS + 1);
-        }
-#pragma unroll
-        for (int u = 0; u < CPS; ++u) {
-            const int c = c0 + u;
-            const int q = u % PF;
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-                *reinterpret_cast<u32x4*>(wtile + (RPI * i + half) * XP + col) = wr[q][i];
-            load_w(q, c + PF);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                Frag<bf16_t> wf[RT];
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) wf[rt].load(wtile + (rt * 16 + ln) * XP + 32 * ks + 8 * lg);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    Frag<bf16_t> xf;
-                    xf.load(xs + (mt * 16 + ln) * SP + u * CH + 32 * ks + 8 * lg);
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) mma(acc[rt][mt], xf, wf[rt]);
-                }
-            }
-            // the next chunk's transpose reuses this wave's tile: order the reads before it
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-    }
-    __syncthreads();
-    tile_epilogue<MT, RT, NWG, EPI, NW>(P, bt, acc, m0, Mb, tile, n_wave, wave, lane, nullptr,
-                                        red_v, red_i);
-}
-
-#ifndef MEDUSA_SLAB_NW
-#define MEDUSA_SLAB_NW 8
-#endif
-#ifndef MEDUSA_SLAB_RT
-#define MEDUSA_SLAB_RT 4
-#endif
-#ifndef MEDUSA_SLAB_PF
-#define MEDUSA_SLAB_PF 2
-#endif
-#ifndef MEDUSA_SLAB
-#define MEDUSA_SLAB 1
-#endif
-constexpr int kSlabNw = MEDUSA_SLAB_NW;
-constexpr int kSlabRt = MEDUSA_SLAB_RT;
-constexpr int kSlabPf = MEDUSA_SLAB_PF;
-
-// The slab argmax kernel: bf16, contraction a multiple of the 512-column slab, more than
-// 64 input rows.  Measured in the step: dense 256-node tree (256 rows) 472 -> 413 us against
-// the row-streaming kernel; at 64 rows two row-streaming workgroups per CU hide latency
-// better (170 against 176 us).
-__host__ bool slab_argmax_eligible(medusa_dtype dt, int epi, int M, int K) {
-    return MEDUSA_SLAB && dt == MEDUSA_BF16 && (epi == EPI_ARGMAX || epi == EPI_TYPICAL) &&
-           M > 64 && K % kSlab == 0;
 }
 
 // Sum the contraction slices of every (m, n) in slice order and apply the store epilogue:
@@ -1662,7 +1481,6 @@ bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
 int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
     if (epi == EPI_PARTIAL) return kWavePartialRows;
-    if (slab_argmax_eligible(dt, epi, M, K)) return kSlabNw * 16 * kSlabRt;
     if (rowstream_eligible(dt, epi, M, K))
         return epi == EPI_ARGMAX || epi == EPI_TYPICAL ? kRsWavesArgmax * 16 * kRsRtwArgmax
                                                        : kWaves * 16 * kRsRtw;
@@ -1711,19 +1529,44 @@ bool gemv_eligible(medusa_dtype dt, int epi, const GemmBatch& bt) {
 
 }  // namespace
 
+// LDS bytes of a row-streaming workgroup: X chunk (plus a spare row slot), the waves' W
+// tiles, the per-wave epilogue reductions.
+template <int MT, int RTW, int CH, int NWV>
+constexpr size_t rowstream_lds() {
+    return (size_t)(MT * 16 * (CH + 8) + 8) * 2 + (size_t)NWV * 16 * RTW * (CH + 8) * 2 +
+           (size_t)NWV * MT * 16 * 8;
+}
+
 template <int MT, int EPI, int RTW, int PF, int CH, int NWV>
 hipError_t launch_rowstream_t(GemmBatch& bt, hipStream_t stream) {
+    auto kern = gemm_rowstream_kernel<MT, EPI, RTW, PF, CH, NWV>;
+    constexpr size_t lds = rowstream_lds<MT, RTW, CH, NWV>();
+    if (lds > 65536) {
+        static bool attr = false;
+        if (!attr) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            attr = true;
+        }
+    }
     const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
-    hipLaunchKernelGGL((gemm_rowstream_kernel<MT, EPI, RTW, PF, CH, NWV>),
-                       dim3(bt.total_tiles * n_mb), dim3(NWV * kWave), 0, stream, bt);
+    hipLaunchKernelGGL(kern, dim3(bt.total_tiles * n_mb), dim3(NWV * kWave), lds, stream, bt);
     return hipGetLastError();
 }
 
+// Input-row blocks: up to 64 rows in one block of the smallest fitting size; above that,
+// blocks of 128 rows.  Every block streams the workgroup's weight rows again, so larger
+// blocks cut that traffic: against 64-row blocks the dense 256-node tree at the 8B shape
+// verifies in 334 us instead of 469 (411 with a former kernel that staged the inputs in
+// 512-column slabs), and batched 70B in 323 instead of 378.  256-row blocks need 240
+// VGPRs, one workgroup per CU, and measured 384 us.
 template <int EPI, int RTW, int PF, int CH, int NWV>
 hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
     if (bt.M <= 16) return launch_rowstream_t<1, EPI, RTW, PF, CH, NWV>(bt, stream);
     if (bt.M <= 32) return launch_rowstream_t<2, EPI, RTW, PF, CH, NWV>(bt, stream);
-    return launch_rowstream_t<4, EPI, RTW, PF, CH, NWV>(bt, stream);
+    if (bt.M <= 64) return launch_rowstream_t<4, EPI, RTW, PF, CH, NWV>(bt, stream);
+    return launch_rowstream_t<8, EPI, RTW, PF, CH, NWV>(bt, stream);
 }
 
 hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
@@ -1732,22 +1575,6 @@ hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
     if (epi == EPI_TYPICAL)
         return launch_rowstream_m<EPI_TYPICAL, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
     return launch_rowstream_m<EPI_ARGMAX, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
-}
-
-template <int EPI>
-hipError_t launch_slab_argmax(GemmBatch& bt, hipStream_t stream) {
-    auto kern = gemm_slab_argmax_kernel<kSlabNw, kSlabRt, kSlabPf, EPI>;
-    const size_t lds = slab_argmax_lds(kSlabNw, kSlabRt);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
-    const int n_mb = (bt.M + 63) / 64;
-    hipLaunchKernelGGL(kern, dim3(bt.total_tiles * n_mb), dim3(kSlabNw * kWave), lds, stream, bt);
-    return hipGetLastError();
 }
 
 // Row-streaming MFMA path: bf16, contraction a multiple of its 256-wide chunk, argmax or
@@ -1871,9 +1698,6 @@ hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& bt, hipStream_t
 }
 
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& bt, hipStream_t stream) {
-    if (slab_argmax_eligible(dt, epi, bt.M, bt.K))
-        return epi == EPI_TYPICAL ? launch_slab_argmax<EPI_TYPICAL>(bt, stream)
-                                  : launch_slab_argmax<EPI_ARGMAX>(bt, stream);
     if (rowstream_eligible(dt, epi, bt.M, bt.K)) return launch_rowstream(epi, bt, stream);
     if (gemv_eligible(dt, epi, bt))
         return epi == EPI_TOPS ? launch_gemv_k<EPI_TOPS>(bt, stream) : launch_gemv_k<EPI_STORE>(bt, stream);
