@@ -300,16 +300,23 @@ def blas_threads() -> int:
         return 1
 
 
-def cpu_baseline(inp, oplan) -> dict:
-    """The oracle, as it stands, on one full step of the same workload (host cores)."""
+def cpu_baseline(inp, oplan, reps: int = 3) -> dict:
+    """The oracle, as it stands, on whole steps of the same workload (host cores): one
+    warm-up step, then the median of `reps` timed steps."""
+    import statistics
     import oracle
-    t0 = time.perf_counter()
     res = oracle.step(inp, oplan)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.step(inp, oplan)
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
     cores, model = cpu_info()
     return {"value": 1.0 / dt, "unit": "steps/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"one whole step (all parts) of the same workload and seed, fp64 numpy "
-                      f"({dt:.1f} s); host {model}, {cores} cores visible",
+            "sample": f"whole steps (all parts) of the same workload and seed, fp64 numpy: "
+                      f"one warm-up, median of {reps} ({dt:.1f} s each); host {model}, "
+                      f"{cores} cores visible",
             "seconds_per_step": dt, "accept_len": [int(a) for a in res.accept_len]}
 
 
