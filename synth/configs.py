@@ -150,6 +150,12 @@ CONFIGS = {
         Lcap=256,
         sigma_lm=_inv_sqrt(512), sigma_w1=_inv_sqrt(512), sigma_b1=_inv_sqrt(512),
         sigma_w2=_inv_sqrt(512), sigma_proxy=_inv_sqrt(512)),
+    # the largest batch the heads accept (64 sequences), ragged prefixes from empty to full
+    "small_b64": Config(
+        name="small_b64", B=64, H=256, V=1000, K=3, s=(2, 3, 3), tree="full", tree_s=(2, 3),
+        n_nodes=9, Hq=4, Hkv=2, d=64, L_range=(0, 64), Lcap=64,
+        sigma_lm=_inv_sqrt(256), sigma_w1=_inv_sqrt(256), sigma_b1=_inv_sqrt(256),
+        sigma_w2=_inv_sqrt(256), sigma_proxy=_inv_sqrt(256)),
     # the verifier with rotary positions (base 10000): ragged prefixes including an empty
     # one, and a loop case whose rounds move the positions on
     "small_rope": Config(

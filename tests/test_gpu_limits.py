@@ -1,7 +1,8 @@
-"""GPU parity at the library's limits, at a small shape: eight heads (the most allowed),
+"""GPU parity at the library's limits, at small shapes: eight heads (the most allowed),
 top-64 on the first (the largest top-k), and a 1024-node tree (the largest plan: depth 8,
 sixteen mask words, 2048 verified rows over two sequences) with an empty and a ragged
-prefix.  The inputs are not planted (no planting opens a margin at 2048 nodes), so each
+prefix; and the largest batch, 64 sequences.  The inputs are not planted (planting opens
+no margins at 2048 nodes, nor across 64 sequences sharing the heads), so each
 node's argmax may take either side of a near-tie and the accept results must follow from
 the device's own decisions; the heads' top-65 gaps are checked to be far above the fp32
 rounding of the device's logits, so their top-k is exact."""
@@ -37,4 +38,24 @@ def test_limits_step(dev):
             assert np.min(v[:-1] - v[1:]) >= 1e-4, "the draw has a near-tie in a head's top-k"
     _, got = run_gpu(inp, dev, keep_logits=False, keep_u=False)
     compare_step(inp, got, ref, plan=plan, check_logits=False, check_u=False)
+    say(f"    accept {got['accept_len'].tolist()}")
+
+
+def test_batch64_step(dev):
+    """The largest batch the heads accept: 64 sequences (row-streaming heads over four
+    16-row blocks, 576 verified rows), prefixes from empty to the full cache."""
+    say("[limits: B=64]")
+    inp = make_inputs("small_b64", 2)
+    cfg = inp.cfg
+    assert int(inp.prefix_lens.min()) == 0 and int(inp.prefix_lens.max()) == cfg.Lcap
+    plan = oracle_plan(inp)
+    ref = oracle.step(inp, plan)
+    for b in range(cfg.B):
+        r = np.sort(ref.root_logits[b])[-2:]
+        assert r[1] - r[0] >= 1e-4, "the draw has a near-tie at a root"
+        for k in range(cfg.K):
+            v = np.sort(ref.head_logits[b, k])[::-1][: cfg.s[k] + 1]
+            assert np.min(v[:-1] - v[1:]) >= 1e-4, "the draw has a near-tie in a head's top-k"
+    _, got = run_gpu(inp, dev, keep_logits=True)
+    compare_step(inp, got, ref, plan=plan)
     say(f"    accept {got['accept_len'].tolist()}")
