@@ -1439,6 +1439,128 @@ hipError_t launch_t(GemmBatch& bt, hipStream_t stream) {
     return hipGetLastError();
 }
 
+
+// Tiled MFMA GEMM with the store epilogue, for many input rows (the verifier's projections
+// from 384 verified rows, where the contraction becomes compute-heavy: 512 rows at the
+// 70B shape are 512 flops per weight byte).  A workgroup of four waves owns a
+// (32*MTW) x (32*RTW) tile of Y = X W^T, the waves in a 2 x 2 arrangement, and walks the
+// contraction in 64-wide chunks: the chunk's X and W rows are loaded into registers one
+// chunk ahead (8 lanes x 16 B per row per instruction; gathered X rows without a source
+// read row 0 and are zeroed), stored into LDS, and read back in the MFMA operand layout.
+// The workgroups sharing a W tile are consecutive in the XCD-aware numbering, so the tile
+// streams from HBM once and from L2 for the others.  No contraction split: the epilogue
+// writes the output directly.
+template <int MTW, int RTW>
+__global__ __launch_bounds__(kThreads) void gemm_tile_store_kernel(const GemmBatch bt) {
+    constexpr int TM = 32 * MTW;                // input rows per tile
+    constexpr int TN = 32 * RTW;                // weight rows per tile
+    constexpr int CH = 64;
+    constexpr int XP = CH + 8;
+    constexpr int LPR = CH / 8;                 // lanes per row per load instruction
+    constexpr int RPI = kThreads / LPR;         // rows per workgroup load instruction
+    constexpr int XL = TM / RPI;                // X loads per thread per chunk
+    constexpr int WL = TN / RPI;                // W loads per thread per chunk
+    static_assert(XL >= 1 && WL >= 1 && XL * RPI == TM && WL * RPI == TN, "tile rows");
+    __shared__ __align__(16) bf16_t xs[TM * XP];
+    __shared__ __align__(16) bf16_t ws[TN * XP];
+
+    const int n_mb = (bt.M + TM - 1) / TM;
+    const int nblocks = bt.total_tiles * n_mb;
+    const int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int mb = bid % n_mb;
+    const int t = bid / n_mb;
+    const GemmProblem& P = bt.p[problem_of(bt, t)];
+    const int tile = t - P.tile_begin;
+    const int K = bt.K;
+    const int N = P.N;
+    const int m0 = mb * TM;
+    const int n0 = tile * TN;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int wm = (wave & 1) * 16 * MTW;       // the wave's rows within the tile
+    const int wn = (wave >> 1) * 16 * RTW;
+
+    const int lrow = threadIdx.x / LPR;         // row of this thread's loads (plus RPI * i)
+    const int lcol = (threadIdx.x % LPR) * 8;
+    const bf16_t* X = static_cast<const bf16_t*>(P.X);
+    const bf16_t* W = static_cast<const bf16_t*>(P.W);
+    const bf16_t* xsrc[XL];
+    bool xok[XL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+        const int m = m0 + lrow + RPI * i;
+        long long r = 0;
+        bool ok = m < bt.M;
+        if (ok) {
+            r = m;
+            if (P.x_rows) {
+                r = P.x_rows[m];
+                ok = r >= 0 && r < bt.x_rows_bound;
+                if (!ok) r = 0;
+            }
+        }
+        xok[i] = ok;
+        xsrc[i] = X + r * P.x_stride + lcol;
+    }
+    const bf16_t* wsrc[WL];
+#pragma unroll
+    for (int i = 0; i < WL; ++i)
+        wsrc[i] = W + (long long)min(n0 + lrow + RPI * i, N - 1) * K + lcol;
+
+    const int n_ch = K / CH;
+    u32x4 xr[XL], wr[WL];
+    auto load = [&](int c) {
+        const int kc = min(c, n_ch - 1) * CH;
+#pragma unroll
+        for (int i = 0; i < XL; ++i) xr[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kc);
+#pragma unroll
+        for (int i = 0; i < WL; ++i) wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[i] + kc));
+    };
+
+    floatx4 acc[RTW][MTW];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    load(0);
+    for (int c = 0; c < n_ch; ++c) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < XL; ++i)
+            *reinterpret_cast<u32x4*>(xs + (lrow + RPI * i) * XP + lcol) = xok[i] ? xr[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < WL; ++i)
+            *reinterpret_cast<u32x4*>(ws + (lrow + RPI * i) * XP + lcol) = wr[i];
+        __syncthreads();
+        load(c + 1);
+#pragma unroll
+        for (int ks = 0; ks < CH; ks += 32) {
+            Frag<bf16_t> wf[RTW];
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) wf[rt].load(ws + (wn + rt * 16 + ln) * XP + ks + 8 * lg);
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) {
+                Frag<bf16_t> xf;
+                xf.load(xs + (wm + mt * 16 + ln) * XP + ks + 8 * lg);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) mma(acc[rt][mt], xf, wf[rt]);
+            }
+        }
+    }
+    store_epilogue<bf16_t, MTW, RTW>(P, bt, acc, m0 + wm, n0 + wn, ln, lg);
+}
+
+template <int MTW, int RTW>
+hipError_t launch_tile_store(GemmBatch& bt, hipStream_t stream) {
+    const int n_mb = (bt.M + 32 * MTW - 1) / (32 * MTW);
+    hipLaunchKernelGGL((gemm_tile_store_kernel<MTW, RTW>), dim3(bt.total_tiles * n_mb),
+                       dim3(kThreads), 0, stream, bt);
+    return hipGetLastError();
+}
+
 template <typename T, int MT, int RT>
 hipError_t launch_splitk(GemmBatch& bt, hipStream_t stream) {
     const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
@@ -1450,8 +1572,23 @@ hipError_t launch_splitk(GemmBatch& bt, hipStream_t stream) {
 // Weight rows per workgroup of the split-contraction store kernel.
 int splitk_rt(int M) { return M <= 16 ? 2 : 1; }
 
+// The tiled store GEMM (128 x 128 tiles) serves bf16 from 384 input rows.  Measured at
+// the 70B shape (512 rows): q/k/v 364 -> 191 us and the output projection 300 -> 192 us
+// against the slice kernel.  Below 384 rows the slice kernel stays: with 64 x 64 tiles the
+// dense tree's 256 rows took 63 / 65 us against 63 / 46, and 128 x 128 tiles leave most
+// CUs idle there.
+#ifndef MEDUSA_TILE_STORE
+#define MEDUSA_TILE_STORE 1
+#endif
+constexpr int kTileRtw = 4;
+bool tile_store_eligible(medusa_dtype dt, int M, int K) {
+    return MEDUSA_TILE_STORE && dt == MEDUSA_BF16 && M >= 384 && K % 64 == 0;
+}
+
 template <typename T>
 hipError_t launch_store(GemmBatch& bt, hipStream_t stream) {
+    if (tile_store_eligible(sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, bt.M, bt.K))
+        return launch_tile_store<kTileRtw, kTileRtw>(bt, stream);
     if (bt.M <= 16) return launch_splitk<T, 1, 2>(bt, stream);
     if (bt.M <= 32) return launch_splitk<T, 2, 1>(bt, stream);
     return launch_splitk<T, 4, 1>(bt, stream);
@@ -1479,6 +1616,7 @@ hipError_t launch_epi(int epi, GemmBatch& bt, hipStream_t stream) {
 bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
 
 int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
+    if (epi == EPI_STORE && tile_store_eligible(dt, M, K)) return 32 * kTileRtw;
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
     if (epi == EPI_PARTIAL) return kWavePartialRows;
     if (rowstream_eligible(dt, epi, M, K))
@@ -1604,6 +1742,7 @@ size_t cu_partial_lds(int nw, int K, int ks) {
 PartialPlan partial_plan(medusa_dtype dt, int M, int K, const int* Ns, int n) {
     PartialPlan pl{0, 0};
     if (dt != MEDUSA_BF16 || M <= 16 || K % kPartialChunk != 0) return pl;
+    if (tile_store_eligible(dt, M, K)) return pl;       // the tiled store GEMM, no slices
     long long rows = 0;
     bool rows32 = true;
     for (int i = 0; i < n; ++i) {

@@ -7,7 +7,8 @@ count (one case has a zero residual, so node_hidden is the projection alone).  T
 cover each kernel choice: one workgroup per CU (64 rows, 8B-class sizes), row tiles that
 run across the q/k/v boundary, more than 64 rows (several row blocks), fewer than 64, at
 most 16 (direct store kernel), k/v widths that are not a multiple of 32 (single-wave
-kernel) and contraction lengths that are not multiples of 64 (direct store kernel)."""
+kernel), contraction lengths that are not multiples of 64 (direct store kernel), and 384
+rows or more (tiled store kernel, also with widths that end in a partial tile)."""
 import numpy as np
 import pytest
 
@@ -26,6 +27,8 @@ CASES = {
     "rows130": (130, 512, 300, 4, 1, 64),
     "qkv_boundary": (40, 1024, 500, 6, 2, 80),
     "kv_width16": (64, 512, 300, 6, 1, 16),
+    "rows512": (512, 512, 300, 4, 1, 64),
+    "rows400_ragged": (400, 1024, 500, 6, 1, 80),
 }
 
 
