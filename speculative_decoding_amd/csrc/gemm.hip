@@ -1440,29 +1440,38 @@ hipError_t launch_t(GemmBatch& bt, hipStream_t stream) {
 }
 
 
-// Tiled MFMA GEMM with the store epilogue, for many input rows (the verifier's projections
-// from 384 verified rows, where the contraction becomes compute-heavy: 512 rows at the
-// 70B shape are 512 flops per weight byte).  A workgroup of four waves owns a
-// (32*MTW) x (32*RTW) tile of Y = X W^T, the waves in a 2 x 2 arrangement, and walks the
-// contraction in 64-wide chunks: the chunk's X and W rows are loaded into registers one
-// chunk ahead (8 lanes x 16 B per row per instruction; gathered X rows without a source
-// read row 0 and are zeroed), stored into LDS, and read back in the MFMA operand layout.
-// The workgroups sharing a W tile are consecutive in the XCD-aware numbering, so the tile
-// streams from HBM once and from L2 for the others.  No contraction split: the epilogue
-// writes the output directly.
-template <int MTW, int RTW>
-__global__ __launch_bounds__(kThreads) void gemm_tile_store_kernel(const GemmBatch bt) {
-    constexpr int TM = 32 * MTW;                // input rows per tile
-    constexpr int TN = 32 * RTW;                // weight rows per tile
+// Tiled MFMA GEMM for many input rows: the verifier's projections from 384 verified rows
+// (store epilogue; the contraction is compute-heavy there: 512 rows at the 70B shape are
+// 512 flops per weight byte) and lm_head over more than 64 verified rows (argmax
+// epilogue).  A workgroup of WM x WN waves owns a (16*WM*MTW) x (16*WN*RTW) tile of
+// Y = X W^T, each wave a (16*MTW) x (16*RTW) block, and walks the contraction in 64-wide
+// chunks: the chunk's X and W rows are loaded into registers one chunk ahead (8 lanes x
+// 16 B per row per instruction; gathered X rows without a source read row 0 and are
+// zeroed), stored into LDS, and read back in the MFMA operand layout.  The workgroups
+// sharing a W tile are neighbours in the XCD-aware numbering, so the tile leaves HBM once.
+// No contraction split.  The LDS layout is tile_lds()'s.
+template <int WM, int WN, int MTW, int RTW>
+constexpr size_t tile_lds() {
+    return (size_t)(16 * WM * MTW + 16 * WN * RTW) * (64 + 8) * 2 + (size_t)WN * 16 * WM * MTW * 8;
+}
+
+template <int WM, int WN, int MTW, int RTW, int EPI>
+__global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBatch bt) {
+    constexpr int NT = WM * WN * kWave;
+    constexpr int TM = 16 * WM * MTW;           // input rows per tile
+    constexpr int TN = 16 * WN * RTW;           // weight rows per tile
     constexpr int CH = 64;
     constexpr int XP = CH + 8;
     constexpr int LPR = CH / 8;                 // lanes per row per load instruction
-    constexpr int RPI = kThreads / LPR;         // rows per workgroup load instruction
+    constexpr int RPI = NT / LPR;               // rows per workgroup load instruction
     constexpr int XL = TM / RPI;                // X loads per thread per chunk
     constexpr int WL = TN / RPI;                // W loads per thread per chunk
     static_assert(XL >= 1 && WL >= 1 && XL * RPI == TM && WL * RPI == TN, "tile rows");
-    __shared__ __align__(16) bf16_t xs[TM * XP];
-    __shared__ __align__(16) bf16_t ws[TN * XP];
+    extern __shared__ __align__(16) unsigned char tile_smem[];
+    bf16_t* xs = reinterpret_cast<bf16_t*>(tile_smem);          // [TM][XP]
+    bf16_t* ws = xs + TM * XP;                                  // [TN][XP]
+    auto& red_v = *reinterpret_cast<float (*)[WN][TM]>(ws + TN * XP);
+    auto& red_i = *reinterpret_cast<int (*)[WN][TM]>(&red_v[WN][0]);
 
     const int n_mb = (bt.M + TM - 1) / TM;
     const int nblocks = bt.total_tiles * n_mb;
@@ -1479,8 +1488,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_store_kernel(const GemmBat
     const int lane = threadIdx.x & 63;
     const int ln = lane & 15;
     const int lg = lane >> 4;
-    const int wm = (wave & 1) * 16 * MTW;       // the wave's rows within the tile
-    const int wn = (wave >> 1) * 16 * RTW;
+    const int wmi = wave % WM;                  // the wave's block within the tile
+    const int wni = wave / WM;
+    const int wm = wmi * 16 * MTW;
+    const int wn = wni * 16 * RTW;
 
     const int lrow = threadIdx.x / LPR;         // row of this thread's loads (plus RPI * i)
     const int lcol = (threadIdx.x % LPR) * 8;
@@ -1516,7 +1527,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_store_kernel(const GemmBat
 #pragma unroll
         for (int i = 0; i < XL; ++i) xr[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kc);
 #pragma unroll
-        for (int i = 0; i < WL; ++i) wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[i] + kc));
+        for (int i = 0; i < WL; ++i)
+            wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[i] + kc));
     };
 
     floatx4 acc[RTW][MTW];
@@ -1550,14 +1562,76 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_store_kernel(const GemmBat
             }
         }
     }
-    store_epilogue<bf16_t, MTW, RTW>(P, bt, acc, m0 + wm, n0 + wn, ln, lg);
+    if (EPI == EPI_STORE) {
+        store_epilogue<bf16_t, MTW, RTW>(P, bt, acc, m0 + wm, n0 + wn, ln, lg);
+        return;
+    }
+    // EPI_ARGMAX: optional fp32 logits, then each wave's best (value, id) per row over its
+    // columns, and the WN waves that share the rows combine in a fixed order; one partial
+    // per (row, tile)
+    if (P.logits) {
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const int n = n0 + wn + rt * 16 + ln;
+            if (n >= N) continue;
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + wm + mt * 16 + 4 * lg + r;
+                    if (m < bt.M) P.logits[(long long)m * P.logits_ld + n] = acc[rt][mt][r];
+                }
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
+                const int n = n0 + wn + rt * 16 + ln;
+                const float v = n < N ? acc[rt][mt][r] : -INFINITY;
+                const int id = n < N ? n : INT_MAX;
+                if (better(v, id, bv, bi)) { bv = v; bi = id; }
+            }
+            row_best(bv, bi);
+            if (ln == 0) {
+                red_v[wni][wm + mt * 16 + 4 * lg + r] = bv;
+                red_i[wni][wm + mt * 16 + 4 * lg + r] = bi;
+            }
+        }
+    __syncthreads();
+    const int Mb = min(bt.M - m0, TM);
+    for (int m = threadIdx.x; m < Mb; m += NT) {
+        float bv = red_v[0][m];
+        int bi = red_i[0][m];
+#pragma unroll
+        for (int w = 1; w < WN; ++w)
+            if (better(red_v[w][m], red_i[w][m], bv, bi)) { bv = red_v[w][m]; bi = red_i[w][m]; }
+        const long long o = (long long)(m0 + m) * P.n_tiles + tile;
+        P.part_val[o] = bv;
+        P.part_idx[o] = bi;
+    }
 }
 
-template <int MTW, int RTW>
-hipError_t launch_tile_store(GemmBatch& bt, hipStream_t stream) {
-    const int n_mb = (bt.M + 32 * MTW - 1) / (32 * MTW);
-    hipLaunchKernelGGL((gemm_tile_store_kernel<MTW, RTW>), dim3(bt.total_tiles * n_mb),
-                       dim3(kThreads), 0, stream, bt);
+template <int WM, int WN, int MTW, int RTW, int EPI>
+hipError_t launch_tile(GemmBatch& bt, hipStream_t stream) {
+    auto kern = gemm_tile_kernel<WM, WN, MTW, RTW, EPI>;
+    constexpr size_t lds = tile_lds<WM, WN, MTW, RTW>();
+    if (lds > 65536) {
+        static bool attr = false;
+        if (!attr) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            attr = true;
+        }
+    }
+    constexpr int TM = 16 * WM * MTW;
+    const int n_mb = (bt.M + TM - 1) / TM;
+    hipLaunchKernelGGL(kern, dim3(bt.total_tiles * n_mb), dim3(WM * WN * kWave), lds, stream, bt);
     return hipGetLastError();
 }
 
@@ -1588,7 +1662,7 @@ bool tile_store_eligible(medusa_dtype dt, int M, int K) {
 template <typename T>
 hipError_t launch_store(GemmBatch& bt, hipStream_t stream) {
     if (tile_store_eligible(sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, bt.M, bt.K))
-        return launch_tile_store<kTileRtw, kTileRtw>(bt, stream);
+        return launch_tile<2, 2, kTileRtw, kTileRtw, EPI_STORE>(bt, stream);
     if (bt.M <= 16) return launch_splitk<T, 1, 2>(bt, stream);
     if (bt.M <= 32) return launch_splitk<T, 2, 1>(bt, stream);
     return launch_splitk<T, 4, 1>(bt, stream);
@@ -1699,11 +1773,17 @@ hipError_t launch_rowstream_t(GemmBatch& bt, hipStream_t stream) {
 // verifies in 334 us instead of 469 (411 with a former kernel that staged the inputs in
 // 512-column slabs), and batched 70B in 323 instead of 378.  256-row blocks need 240
 // VGPRs, one workgroup per CU, and measured 384 us.
+// Greedy verification past 64 rows runs on the tiled kernel: 128 input rows x 256 weight
+// rows per workgroup (2 x 4 waves, two workgroups per CU), the same 256-row tiles as the
+// row-streaming kernel.  Dense 256-node tree 333 -> 319 us, batched 70B 320 -> 313 us,
+// 341 nodes at the 8B shape 1.40 -> 1.37 ms per step; 256 x 256 tiles (16 waves) and
+// 256 x 256 with 8 waves of 256 accumulators did no better overall.
 template <int EPI, int RTW, int PF, int CH, int NWV>
 hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
     if (bt.M <= 16) return launch_rowstream_t<1, EPI, RTW, PF, CH, NWV>(bt, stream);
     if (bt.M <= 32) return launch_rowstream_t<2, EPI, RTW, PF, CH, NWV>(bt, stream);
     if (bt.M <= 64) return launch_rowstream_t<4, EPI, RTW, PF, CH, NWV>(bt, stream);
+    if (EPI == EPI_ARGMAX) return launch_tile<2, 4, 4, 4, EPI_ARGMAX>(bt, stream);
     return launch_rowstream_t<8, EPI, RTW, PF, CH, NWV>(bt, stream);
 }
 
