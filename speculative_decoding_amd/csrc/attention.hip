@@ -4,9 +4,9 @@
 //
 // Work split.  For one sequence b and one kv head g the query rows are the N*G
 // (node, query head) pairs of that group; they share every key, so they are the M side of
-// two MFMA contractions (scores and the value sum).  A workgroup takes 64 query rows (16
-// per wave) and one key range: a chunk of the prefix, or the tree keys.  Each 64-key
-// block is staged in LDS (K row-major, V transposed) and shared by the four waves.  Scores
+// two MFMA contractions (scores and the value sum).  A workgroup takes 64 or 128 query rows
+// (16 per wave) and one key range: a chunk of the prefix, or the tree keys.  Each 64-key
+// block is staged in LDS (K row-major, V transposed) and shared by the waves.  Scores
 // are computed transposed, S^T = K Q^T, so each lane owns one query row; its softmax
 // state stays in registers and the value sum O^T = V^T P^T takes P^T straight from the
 // score registers (the two 16-key score tiles give each lane the eight key slots of one
@@ -25,16 +25,14 @@ namespace medusa {
 namespace {
 
 constexpr int kThreads = 256;     // the combine kernel
-#ifndef MEDUSA_ATTN_WAVES
-#define MEDUSA_ATTN_WAVES 4
-#endif
 // Waves (16 query rows each) per attention workgroup: the K/V blocks staged in LDS are
 // shared by all of them, so more waves mean fewer passes of the same keys through each CU.
 // Measured: 8 waves help at 512 and more query rows per kv head (dense 256-node tree 105 ->
-// 102 us, batched 70B 316 -> 300 us) and cost 3 us at 256 (the 8B tree: 22.5 -> 25.5 us).
-constexpr int kAttnWaves = MEDUSA_ATTN_WAVES;
-constexpr int kAttnRows = 16 * kAttnWaves;
-constexpr int kAttnThreads = kAttnWaves * 64;
+// 102 us, batched 70B 316 -> 300 us) and cost 3 us at 256 (the 8B tree: 22.5 -> 25.5 us),
+// so attn_shape() takes 8 from 512 rows and 4 below.
+constexpr int kAttnWavesSmall = 4;
+constexpr int kAttnWavesLarge = 8;
+constexpr int kAttnLargeRows = 512;
 constexpr int kKeys = 64;          // keys staged per LDS block
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -93,8 +91,10 @@ template <> struct Vt4<float> {
     __device__ static __forceinline__ float elem(const u32x4& v, int e) { return __uint_as_float(v[e]); }
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(const AttnArgs a) {
+template <typename T, int D, int NWV>
+__global__ __launch_bounds__(NWV * 64) void attn_partial_kernel(const AttnArgs a) {
+    constexpr int kAttnThreads = NWV * 64;
+    constexpr int kAttnRows = 16 * NWV;
     constexpr int EPV = 16 / sizeof(T);
     constexpr int KP = D + 8;          // K row pitch (elements)
     constexpr int VP = kKeys + 8;      // V^T row pitch
@@ -362,7 +362,12 @@ hipError_t launch_td(const AttnArgs& a, hipStream_t stream) {
     const AttnShape& s = a.s;
     const int nblocks = s.B * s.Hkv * (s.n_splits + 1) * s.n_qblocks;
     prof_begin("attn_partial", stream);
-    hipLaunchKernelGGL((attn_partial_kernel<T, D>), dim3(nblocks), dim3(kAttnThreads), 0, stream, a);
+    if (s.waves == kAttnWavesLarge)
+        hipLaunchKernelGGL((attn_partial_kernel<T, D, kAttnWavesLarge>), dim3(nblocks),
+                           dim3(kAttnWavesLarge * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_partial_kernel<T, D, kAttnWavesSmall>), dim3(nblocks),
+                           dim3(kAttnWavesSmall * 64), 0, stream, a);
     prof_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -380,14 +385,15 @@ AttnShape attn_shape(int B, int N, int Hq, int Hkv, int d, int Lcap) {
     s.B = B; s.N = N; s.Hq = Hq; s.Hkv = Hkv; s.d = d; s.Lcap = Lcap;
     s.G = Hq / Hkv;
     s.rows = N * s.G;
-    s.n_qblocks = (s.rows + kAttnRows - 1) / kAttnRows;
+    s.waves = s.rows >= kAttnLargeRows ? kAttnWavesLarge : kAttnWavesSmall;
+    s.n_qblocks = (s.rows + 16 * s.waves - 1) / (16 * s.waves);
     // Split the prefix so that (a) the partial outputs (rows * d fp32 per split) stay
     // below about half the K/V bytes they summarise and (b) the grid still covers the
     // chip when there are few (sequence, kv head, query block) triples.
     const int max_splits = Lcap > 0 ? (Lcap + kKeys - 1) / kKeys : 1;
     int splits = Lcap / (2 * s.rows);
     const int base = B * Hkv * s.n_qblocks;
-    const int fill_blocks = 2048 / kAttnWaves;        // about 2048 waves in flight
+    const int fill_blocks = 2048 / s.waves;           // about 2048 waves in flight
     const int fill = (fill_blocks + base - 1) / base;
     if (splits < fill) splits = fill;
     if (splits < 1) splits = 1;

@@ -159,7 +159,8 @@ struct AttnShape {
     int B, N, Hq, Hkv, d, Lcap;
     int G;          // Hq / Hkv
     int rows;       // N * G query rows per (sequence, kv head)
-    int n_qblocks;  // ceil(rows / 64)
+    int waves;      // waves (16 query rows each) per workgroup
+    int n_qblocks;  // ceil(rows / (16 * waves))
     int chunk;      // prefix keys per split (multiple of 64)
     int n_splits;   // prefix splits; one more slot holds the tree keys
 };
