@@ -109,3 +109,25 @@ def test_advance_overflow_changes_nothing(dev):
     for k, v in before.items():
         assert torch.equal(w[k], v), f"{k} changed"
     assert torch.equal(st.root_ids, root)
+
+
+def test_root_only_loop_is_greedy_decoding(dev):
+    """With a root-only tree every round verifies one token and emits one: the loop is plain
+    greedy decoding, token for token, run through the same kernels."""
+    import torch
+    from speculative_decoding_amd import medusa as M
+    from speculative_decoding_amd.step import Dims, MedusaStep, device_weights
+    say("[decode loop, root-only tree]")
+    rounds = 6
+    inp = planted("small_loop", 1)
+    plan = M.medusa_tree_plan_from_accuracy(inp.acc, inp.cfg.tree_s, 1).upload(dev)
+    st = MedusaStep(Dims.from_config(inp.cfg), device_weights(inp, dev), plan, dev)
+    root0, lens, toks, over = st.decode(rounds)
+    torch.cuda.synchronize()
+    assert int(over.max().item()) == 0 and int(lens.max().item()) == 0
+    streams = st.streams(lens, toks)
+    for b in range(inp.cfg.B):
+        g, _, lg = oracle.greedy_decode(inp, b, int(root0[b].item()), rounds)
+        top2 = np.sort(lg, axis=1)[:, -2:]
+        assert (top2[:, 1] - top2[:, 0]).min() >= 2e-2, "seed has a near-tie in its greedy stream"
+        exact(f"sequence {b} stream", streams[b], g)

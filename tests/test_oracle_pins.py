@@ -553,3 +553,16 @@ def test_rope_depends_on_relative_position_only():
         np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-9)
         np.testing.assert_allclose(np.linalg.norm(oracle.rope(q, np.array(m), 10000.0), axis=-1),
                                    np.linalg.norm(q, axis=-1), rtol=1e-13)
+
+
+def test_root_only_decode_loop_is_greedy_decoding():
+    """A root-only tree accepts nothing and emits the root's argmax each round: the loop
+    reduces to plain greedy decoding."""
+    from tests import planting
+    inp = planting.planted_inputs("small_loop", 1)
+    plan = oracle.plan_from_accuracy(inp.acc, inp.cfg.tree_s, 1)
+    root0, streams, res = oracle.decode_loop(inp, plan, 5)
+    assert all(int(r.accept_len.max()) == 0 for r in res)
+    for b in range(inp.cfg.B):
+        g, _, _ = oracle.greedy_decode(inp, b, int(root0[b]), 5)
+        assert streams[b].tolist() == g.tolist()
