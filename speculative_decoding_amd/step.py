@@ -171,6 +171,32 @@ class MedusaStep:
                          self.node_hidden, w["k_cache"], w["v_cache"], w["prefix_lens"], w["h"],
                          self.root_ids, overflow)
 
+    # ---- the decode loop's state: everything a round reads that earlier rounds changed
+    LOOP_STATE = ("k_cache", "v_cache", "prefix_lens", "h")
+
+    def loop_state(self) -> Dict[str, "object"]:
+        """Host copies of the loop state: the KV caches, prefix lengths, last hidden states
+        (the weights dict's entries) and the next roots.  With the weights, it is all a
+        later round needs."""
+        out = {k: self.w[k].detach().cpu().clone() for k in self.LOOP_STATE}
+        out["root_ids"] = self.root_ids.detach().cpu().clone()
+        return out
+
+    def load_loop_state(self, state: Dict[str, "object"]) -> None:
+        """Restore loop_state() into this step's buffers (same shapes); the next run() with
+        bootstrap_root=False continues from there."""
+        for k in self.LOOP_STATE:
+            self.w[k].copy_(state[k])
+        self.root_ids.copy_(state["root_ids"])
+
+    def save_loop_state(self, path: str) -> None:
+        from safetensors.torch import save_file
+        save_file({k: v.contiguous() for k, v in self.loop_state().items()}, path)
+
+    def restore_loop_state(self, path: str) -> None:
+        from safetensors.torch import load_file
+        self.load_loop_state(load_file(path))
+
     def decode(self, steps: int, bootstrap_root: bool = True):
         """``steps`` rounds of run() + advance(), all enqueued without a host
         synchronisation.  Returns device tensors: the first roots [B], and per round the

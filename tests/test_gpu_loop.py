@@ -131,3 +131,28 @@ def test_root_only_loop_is_greedy_decoding(dev):
         top2 = np.sort(lg, axis=1)[:, -2:]
         assert (top2[:, 1] - top2[:, 0]).min() >= 2e-2, "seed has a near-tie in its greedy stream"
         exact(f"sequence {b} stream", streams[b], g)
+
+
+def test_loop_resumes_from_saved_state(dev, tmp_path):
+    """Save the loop state after two rounds (safetensors), finish the loop, then restore the
+    state into a fresh step over the original inputs: the remaining rounds emit the same
+    tokens."""
+    import torch
+    say("[decode loop, save and resume]")
+    inp = planted("small_loop", 3)
+    st, _ = _gpu_step(inp, dev)
+    st.decode(2)
+    torch.cuda.synchronize()
+    path = str(tmp_path / "loop_state.safetensors")
+    st.save_loop_state(path)
+    _, lens, toks, _ = st.decode(3, bootstrap_root=False)
+    torch.cuda.synchronize()
+    want = st.streams(lens, toks)
+
+    fresh, _ = _gpu_step(inp, dev)
+    fresh.restore_loop_state(path)
+    _, lens2, toks2, _ = fresh.decode(3, bootstrap_root=False)
+    torch.cuda.synchronize()
+    got = fresh.streams(lens2, toks2)
+    for b in range(inp.cfg.B):
+        exact(f"sequence {b} resumed stream", got[b], want[b])
