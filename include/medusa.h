@@ -142,7 +142,8 @@ void medusa_tree_plan_destroy(medusa_tree_plan* plan);
  *   u_out    [B, K, H] dtype or NULL (head hidden states; kept in the workspace if NULL)
  *   logits   [B, K+1, V] fp32 or NULL (slot K holds lm_head(h) iff w_lm != NULL)
  * Limits: 1 <= B <= 64, 1 <= K <= MEDUSA_MAX_HEADS, H % 32 == 0, 32 <= H <= 16384,
- * 1 <= V < 2^31. */
+ * 1 <= V <= 262144 (the top-s candidates of at most 2048 vocabulary tiles of 128 rows are
+ * merged per head; a larger V returns MEDUSA_ERR_SHAPE). */
 medusa_status medusa_heads_forward(medusa_dtype dt, int B, int H, int V, int K,
                                    const void* hidden, const void* w1, const void* b1,
                                    const void* w2, const void* w_lm, const int32_t* s,

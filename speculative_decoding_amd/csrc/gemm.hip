@@ -560,13 +560,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
 #define MEDUSA_RS_CHUNK 64
 #endif
 #ifndef MEDUSA_RS_RTW
-#define MEDUSA_RS_RTW 4
+#define MEDUSA_RS_RTW 2
 #endif
 #ifndef MEDUSA_RS_PF
 #define MEDUSA_RS_PF 1
 #endif
+
 constexpr int kRsChunk = MEDUSA_RS_CHUNK;   // contraction chunk per pass
-constexpr int kRsRtw = MEDUSA_RS_RTW;       // 16-row weight tiles per wave (argmax, top-s)
+#ifndef MEDUSA_RS_WAVES_TOPS
+#define MEDUSA_RS_WAVES_TOPS 4
+#endif
+constexpr int kRsRtw = MEDUSA_RS_RTW;       // 16-row weight tiles per wave (top-s)
+constexpr int kRsWavesTops = MEDUSA_RS_WAVES_TOPS;
 constexpr int kRsPf = MEDUSA_RS_PF;         // chunks in flight ahead of the one multiplied
 constexpr int kPartialChunk = 64;           // contraction chunk of the slice kernels
 constexpr int kWavePartialRows = 64;        // weight rows per single-wave slice tile
@@ -1695,7 +1700,7 @@ int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
     if (epi == EPI_PARTIAL) return kWavePartialRows;
     if (rowstream_eligible(dt, epi, M, K))
         return epi == EPI_ARGMAX || epi == EPI_TYPICAL ? kRsWavesArgmax * 16 * kRsRtwArgmax
-                                                       : kWaves * 16 * kRsRtw;
+                                                       : kRsWavesTops * 16 * kRsRtw;
     int rt;
     if (dt == MEDUSA_BF16)
         rt = epi == EPI_TOPS ? StreamCfg<bf16_t, EPI_TOPS>::RT : StreamCfg<bf16_t, EPI_ARGMAX>::RT;
@@ -1783,13 +1788,16 @@ hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
     if (bt.M <= 16) return launch_rowstream_t<1, EPI, RTW, PF, CH, NWV>(bt, stream);
     if (bt.M <= 32) return launch_rowstream_t<2, EPI, RTW, PF, CH, NWV>(bt, stream);
     if (bt.M <= 64) return launch_rowstream_t<4, EPI, RTW, PF, CH, NWV>(bt, stream);
+    // the tiled kernel's weight rows per workgroup (WN * RTW * 16) are the tile size that
+    // gemm_rows_per_tile() reports, which sizes the partials and the grid
+    static_assert(EPI != EPI_ARGMAX || 4 * 4 * 16 == NWV * 16 * RTW, "argmax tile rows");
     if (EPI == EPI_ARGMAX) return launch_tile<2, 4, 4, 4, EPI_ARGMAX>(bt, stream);
     return launch_rowstream_t<8, EPI, RTW, PF, CH, NWV>(bt, stream);
 }
 
 hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
     if (epi == EPI_TOPS)
-        return launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunk, kWaves>(bt, stream);
+        return launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunk, kRsWavesTops>(bt, stream);
     if (epi == EPI_TYPICAL)
         return launch_rowstream_m<EPI_TYPICAL, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
     return launch_rowstream_m<EPI_ARGMAX, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);

@@ -106,6 +106,11 @@ def test_heads_error_paths():
     assert _heads(hidden=FAKE + 8) == 2                    # misaligned
     assert _heads(ws=None) == 5
     assert _heads(ws_bytes=16) == 5
+    # at most 2048 vocabulary tiles of 128 rows per head, on every kernel path
+    for dt in (0, 1):
+        for B in (1, 2, 3, 8, 64):
+            assert _heads(dt=dt, B=B, V=262145) == 2, (dt, B)
+            assert _heads(dt=dt, B=B, V=262144, ws=None) == 5, (dt, B)
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device status; a GPU is visible")
