@@ -26,6 +26,13 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kLdsXBytes = 40960;     // X chunk budget (bytes of LDS)
 constexpr int kSplitUnroll = 4;       // k-steps per load group in the split-contraction kernel
+constexpr int kSplitRowsChunk = 64;   // contraction chunk of its row-contiguous bf16 form
+#ifndef MEDUSA_SPLIT_ROWS
+#define MEDUSA_SPLIT_ROWS 1
+#endif
+#ifndef MEDUSA_SPLIT_ROWS_PF
+#define MEDUSA_SPLIT_ROWS_PF 3
+#endif
 
 // Streaming-kernel tiles: RT 16-row weight tiles per wave, UN k-steps per load group.
 // Chosen by a sweep on MI355X at the 8B shape (RT in {1,2,4} x UN in {2,4,8}): the
@@ -201,6 +208,154 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_store_kernel(const GemmB
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[rt][mt] += red[w][rt][mt][lane];
     store_epilogue<T, MT, RT>(P, bt, acc, m0, n_wave, ln, lg);
+}
+
+// The same split for bf16 when every quarter of the contraction is whole 64-wide chunks:
+// each wave streams its RT*16 weight rows over its quarter with row-contiguous loads (8
+// rows x 128 B per instruction, the pattern that streams HBM fastest) into a wave-private,
+// double-buffered LDS tile and reads the MFMA operands back from it, as the slice kernels
+// do; input fragments come straight from the cache, rows past M are never read.  The four
+// accumulators are summed in wave order through LDS, so the result is the same whichever
+// wave finishes first.
+template <int MT, int RT, int PF>
+__global__ __launch_bounds__(kThreads) void gemm_splitk_rows_kernel(const GemmBatch bt) {
+    constexpr int CH = kSplitRowsChunk;
+    constexpr int KW = kWaves;
+    constexpr int ROWS = 16 * RT;
+    constexpr int XP = CH + 8;                // LDS pitch of a weight row (elements)
+    constexpr int LPR = CH / 8;               // lanes per weight row per load instruction
+    constexpr int RPI = kWave / LPR;          // weight rows per load instruction
+    constexpr int NI = ROWS / RPI;            // weight loads per lane per chunk
+    constexpr int KS = CH / 32;               // MFMA steps per chunk
+    static_assert(ROWS % RPI == 0, "rows per load");
+    __shared__ __align__(16) bf16_t wt_all[KW][2][ROWS * XP];
+    __shared__ floatx4 red[KW - 1][RT][MT][kWave];
+
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    const int nblocks = bt.total_tiles * n_mb;
+    const int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int mb = bid % n_mb;
+    const int t = bid / n_mb;
+    const GemmProblem& P = bt.p[problem_of(bt, t)];
+    const int tile = t - P.tile_begin;
+    const int K = bt.K;
+    const int N = P.N;
+    const int kg = threadIdx.x >> 6;          // this wave's contraction quarter
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int n_wave = tile * ROWS;
+    const int m0 = mb * MT * 16;
+    const int n_ch = K / (CH * KW);           // chunks per quarter (the launch checks K)
+    const int k_lo = kg * n_ch * CH;
+
+    const bf16_t* W = static_cast<const bf16_t*>(P.W);
+    const int half = lane / LPR;
+    const int col = (lane % LPR) * 8;
+    const u32x4* wsrc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int n = min(n_wave + RPI * i + half, N - 1);
+        wsrc[i] = reinterpret_cast<const u32x4*>(W + (long long)n * K + k_lo + col);
+    }
+    const bf16_t* X = static_cast<const bf16_t*>(P.X);
+    const bf16_t* xsrc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = m0 + mt * 16 + ln;
+        long long r = m;
+        bool ok = m < bt.M;
+        if (ok && P.x_rows) {
+            r = P.x_rows[m];
+            ok = r >= 0 && r < bt.x_rows_bound;
+        }
+        xsrc[mt] = ok ? X + r * P.x_stride + k_lo + 8 * lg : nullptr;
+    }
+
+    floatx4 acc[RT][MT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // rings: chunk j in slot j % PF; every load is issued on every path (chunks past the
+    // quarter re-read its last one) so the compiler's wait counts stay exact
+    u32x4 wr[PF][NI];
+    Frag<bf16_t> xr[PF][MT][KS];
+    auto load_w = [&](int p, int c) {
+        const int kc = min(c, n_ch - 1) * CH;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) wr[p][i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
+    };
+    auto load_x = [&](int p, int c) {
+        const int kc = min(c, n_ch - 1) * CH;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (xsrc[mt]) xr[p][mt][ks].load(xsrc[mt] + kc + 32 * ks);
+                else xr[p][mt][ks].zero();
+            }
+    };
+    bf16_t* wt = &wt_all[kg][0][0];
+    auto store_w = [&](int p, int buf) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            *reinterpret_cast<u32x4*>(&wt[buf * ROWS * XP + (RPI * i + half) * XP + col]) = wr[p][i];
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        load_w(p, p);
+        load_x(p, p);
+    }
+    store_w(0, 0);
+    load_w(0, PF);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int c0 = 0; c0 < n_ch; c0 += 2 * PF)
+#pragma unroll
+    for (int u = 0; u < 2 * PF; ++u) {
+        const int c = c0 + u;
+        if (c >= n_ch) break;
+        const int ps = u % PF;                   // slot of chunk c
+        const int pn = (u + 1) % PF;             // slot of chunk c + 1
+        // weights of chunk c+1 into the other buffer, then refill their slot
+        if (c + 1 < n_ch) store_w(pn, (u + 1) & 1);
+        load_w(pn, c + 1 + PF);
+        const bf16_t* wb = wt + (u & 1) * ROWS * XP;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            Frag<bf16_t> wf[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) wf[rt].load(wb + (rt * 16 + ln) * XP + 32 * ks + 8 * lg);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) mma(acc[rt][mt], xr[ps][mt][ks], wf[rt]);
+        }
+        load_x(ps, c + PF);
+        // wave-private buffer: a single-wave ordering point suffices
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    if (kg > 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) red[kg - 1][rt][mt][lane] = acc[rt][mt];
+    }
+    __syncthreads();
+    if (kg != 0) return;
+#pragma unroll
+    for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[rt][mt] += red[w][rt][mt][lane];
+    store_epilogue<bf16_t, MT, RT>(P, bt, acc, m0, n_wave, ln, lg);
 }
 
 // EPI_TYPICAL after the argmax: the tile's softmax sums of every row and the logits of the
@@ -1664,10 +1819,23 @@ bool tile_store_eligible(medusa_dtype dt, int M, int K) {
     return MEDUSA_TILE_STORE && dt == MEDUSA_BF16 && M >= 384 && K % 64 == 0;
 }
 
+template <int MT, int RT>
+hipError_t launch_splitk_rows(GemmBatch& bt, hipStream_t stream) {
+    const int n_mb = (bt.M + MT * 16 - 1) / (MT * 16);
+    hipLaunchKernelGGL((gemm_splitk_rows_kernel<MT, RT, MEDUSA_SPLIT_ROWS_PF>),
+                       dim3(bt.total_tiles * n_mb), dim3(kThreads), 0, stream, bt);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_store(GemmBatch& bt, hipStream_t stream) {
     if (tile_store_eligible(sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, bt.M, bt.K))
         return launch_tile<2, 2, kTileRtw, kTileRtw, EPI_STORE>(bt, stream);
+    if (MEDUSA_SPLIT_ROWS && sizeof(T) == 2 && bt.K % (kSplitRowsChunk * kWaves) == 0) {
+        if (bt.M <= 16) return launch_splitk_rows<1, 2>(bt, stream);
+        if (bt.M <= 32) return launch_splitk_rows<2, 1>(bt, stream);
+        return launch_splitk_rows<4, 1>(bt, stream);
+    }
     if (bt.M <= 16) return launch_splitk<T, 1, 2>(bt, stream);
     if (bt.M <= 32) return launch_splitk<T, 2, 1>(bt, stream);
     return launch_splitk<T, 4, 1>(bt, stream);
