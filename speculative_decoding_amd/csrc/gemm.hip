@@ -1600,22 +1600,27 @@ hipError_t launch_t(GemmBatch& bt, hipStream_t stream) {
 }
 
 
-// Tiled MFMA GEMM for many input rows: the verifier's projections from 384 verified rows
-// (store epilogue; the contraction is compute-heavy there: 512 rows at the 70B shape are
-// 512 flops per weight byte) and lm_head over more than 64 verified rows (argmax
+// Tiled MFMA GEMM for many input rows: the verifier's projections from 128 verified rows
+// (256 x 256 tiles in contraction slices, or 128 x 128 tiles with the store epilogue when
+// one slice is best; the contraction is compute-heavy there: 512 rows at the 70B shape
+// are 512 flops per weight byte) and lm_head over more than 64 verified rows (argmax
 // epilogue).  A workgroup of WM x WN waves owns a (16*WM*MTW) x (16*WN*RTW) tile of
 // Y = X W^T, each wave a (16*MTW) x (16*RTW) block, and walks the contraction in 64-wide
 // chunks: the chunk's X and W rows are loaded into registers one chunk ahead (8 lanes x
 // 16 B per row per instruction; gathered X rows without a source read row 0 and are
 // zeroed), stored into LDS, and read back in the MFMA operand layout.  The workgroups
 // sharing a W tile are neighbours in the XCD-aware numbering, so the tile leaves HBM once.
-// No contraction split.  The LDS layout is tile_lds()'s.
-template <int WM, int WN, int MTW, int RTW>
+// With DB the LDS holds two chunks: chunk c+1 is stored while chunk c is multiplied, and
+// one block barrier per chunk orders them.  EPI_PARTIAL splits the contraction into
+// bt.ksplit slices and writes each slice's fp32 sums to part_val[slice][m][n] for the
+// finalize pass.  The LDS layout is tile_lds()'s.
+template <int WM, int WN, int MTW, int RTW, bool DB = false>
 constexpr size_t tile_lds() {
-    return (size_t)(16 * WM * MTW + 16 * WN * RTW) * (64 + 8) * 2 + (size_t)WN * 16 * WM * MTW * 8;
+    return (size_t)(16 * WM * MTW + 16 * WN * RTW) * (64 + 8) * 2 * (DB ? 2 : 1) +
+           (size_t)WN * 16 * WM * MTW * 8;
 }
 
-template <int WM, int WN, int MTW, int RTW, int EPI>
+template <int WM, int WN, int MTW, int RTW, int EPI, bool DB = false>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBatch bt) {
     constexpr int NT = WM * WN * kWave;
     constexpr int TM = 16 * WM * MTW;           // input rows per tile
@@ -1627,17 +1632,20 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
     constexpr int XL = TM / RPI;                // X loads per thread per chunk
     constexpr int WL = TN / RPI;                // W loads per thread per chunk
     static_assert(XL >= 1 && WL >= 1 && XL * RPI == TM && WL * RPI == TN, "tile rows");
+    constexpr int STAGE = (TM + TN) * XP;       // elements of one chunk's X and W rows
     extern __shared__ __align__(16) unsigned char tile_smem[];
-    bf16_t* xs = reinterpret_cast<bf16_t*>(tile_smem);          // [TM][XP]
-    bf16_t* ws = xs + TM * XP;                                  // [TN][XP]
-    auto& red_v = *reinterpret_cast<float (*)[WN][TM]>(ws + TN * XP);
+    bf16_t* const lds0 = reinterpret_cast<bf16_t*>(tile_smem);   // [DB?2:1][TM+TN][XP]
+    auto& red_v = *reinterpret_cast<float (*)[WN][TM]>(lds0 + STAGE * (DB ? 2 : 1));
     auto& red_i = *reinterpret_cast<int (*)[WN][TM]>(&red_v[WN][0]);
 
     const int n_mb = (bt.M + TM - 1) / TM;
-    const int nblocks = bt.total_tiles * n_mb;
-    const int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int nks = EPI == EPI_PARTIAL ? bt.ksplit : 1;
+    const int nblocks = bt.total_tiles * n_mb * nks;
+    int bid = xcd_logical_block(blockIdx.x, nblocks);
     const int mb = bid % n_mb;
-    const int t = bid / n_mb;
+    bid /= n_mb;
+    const int ksl = bid % nks;                  // contraction slice (EPI_PARTIAL)
+    const int t = bid / nks;
     const GemmProblem& P = bt.p[problem_of(bt, t)];
     const int tile = t - P.tile_begin;
     const int K = bt.K;
@@ -1680,15 +1688,29 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
     for (int i = 0; i < WL; ++i)
         wsrc[i] = W + (long long)min(n0 + lrow + RPI * i, N - 1) * K + lcol;
 
-    const int n_ch = K / CH;
+    // this workgroup's chunks: all of them, or its slice's
+    const int chunks = K / CH;
+    const int per = (chunks + nks - 1) / nks;
+    const int c_lo = min(chunks, ksl * per);
+    const int n_ch = min(chunks, (ksl + 1) * per) - c_lo;
     u32x4 xr[XL], wr[WL];
     auto load = [&](int c) {
-        const int kc = min(c, n_ch - 1) * CH;
+        const int kc = (c_lo + min(c, n_ch - 1)) * CH;
 #pragma unroll
         for (int i = 0; i < XL; ++i) xr[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kc);
 #pragma unroll
         for (int i = 0; i < WL; ++i)
             wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[i] + kc));
+    };
+    auto stash = [&](bf16_t* st) {              // the loaded chunk into one LDS stage
+        bf16_t* xs = st;
+        bf16_t* ws = st + TM * XP;
+#pragma unroll
+        for (int i = 0; i < XL; ++i)
+            *reinterpret_cast<u32x4*>(xs + (lrow + RPI * i) * XP + lcol) = xok[i] ? xr[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < WL; ++i)
+            *reinterpret_cast<u32x4*>(ws + (lrow + RPI * i) * XP + lcol) = wr[i];
     };
 
     floatx4 acc[RTW][MTW];
@@ -1696,18 +1718,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) acc[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    load(0);
-    for (int c = 0; c < n_ch; ++c) {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < XL; ++i)
-            *reinterpret_cast<u32x4*>(xs + (lrow + RPI * i) * XP + lcol) = xok[i] ? xr[i] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < WL; ++i)
-            *reinterpret_cast<u32x4*>(ws + (lrow + RPI * i) * XP + lcol) = wr[i];
-        __syncthreads();
-        load(c + 1);
+    auto multiply = [&](const bf16_t* st) {     // acc += the chunk in one LDS stage
+        const bf16_t* xs = st;
+        const bf16_t* ws = st + TM * XP;
 #pragma unroll
         for (int ks = 0; ks < CH; ks += 32) {
             Frag<bf16_t> wf[RTW];
@@ -1721,9 +1734,52 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
                 for (int rt = 0; rt < RTW; ++rt) mma(acc[rt][mt], xf, wf[rt]);
             }
         }
+    };
+
+    if (n_ch > 0) load(0);
+    if (DB) {
+        // stage c & 1 holds chunk c.  Storing chunk c+1 into the other stage is safe: its
+        // last readers multiplied chunk c-1 before the barrier that ended that iteration.
+        if (n_ch > 0) {
+            stash(lds0);
+            load(1);
+        }
+        __syncthreads();
+        for (int c = 0; c < n_ch; ++c) {
+            multiply(lds0 + (c & 1) * STAGE);
+            if (c + 1 < n_ch) {
+                stash(lds0 + ((c + 1) & 1) * STAGE);
+                load(c + 2);
+            }
+            __syncthreads();
+        }
+    } else {
+        for (int c = 0; c < n_ch; ++c) {
+            __syncthreads();
+            stash(lds0);
+            __syncthreads();
+            load(c + 1);
+            multiply(lds0);
+        }
     }
     if (EPI == EPI_STORE) {
         store_epilogue<bf16_t, MTW, RTW>(P, bt, acc, m0 + wm, n0 + wn, ln, lg);
+        return;
+    }
+    if (EPI == EPI_PARTIAL) {
+        float* part = P.part_val + (long long)ksl * bt.M * N;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            const int n = n0 + wn + rt * 16 + ln;
+            if (n >= N) continue;
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + wm + mt * 16 + 4 * lg + r;
+                    if (m < bt.M) part[(long long)m * N + n] = acc[rt][mt][r];
+                }
+        }
         return;
     }
     // EPI_ARGMAX: optional fp32 logits, then each wave's best (value, id) per row over its
@@ -1776,10 +1832,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
     }
 }
 
-template <int WM, int WN, int MTW, int RTW, int EPI>
+template <int WM, int WN, int MTW, int RTW, int EPI, bool DB = false>
 hipError_t launch_tile(GemmBatch& bt, hipStream_t stream) {
-    auto kern = gemm_tile_kernel<WM, WN, MTW, RTW, EPI>;
-    constexpr size_t lds = tile_lds<WM, WN, MTW, RTW>();
+    auto kern = gemm_tile_kernel<WM, WN, MTW, RTW, EPI, DB>;
+    constexpr size_t lds = tile_lds<WM, WN, MTW, RTW, DB>();
     if (lds > 65536) {
         static bool attr = false;
         if (!attr) {
@@ -1791,7 +1847,9 @@ hipError_t launch_tile(GemmBatch& bt, hipStream_t stream) {
     }
     constexpr int TM = 16 * WM * MTW;
     const int n_mb = (bt.M + TM - 1) / TM;
-    hipLaunchKernelGGL(kern, dim3(bt.total_tiles * n_mb), dim3(WM * WN * kWave), lds, stream, bt);
+    const int nks = EPI == EPI_PARTIAL ? bt.ksplit : 1;
+    hipLaunchKernelGGL(kern, dim3(bt.total_tiles * n_mb * nks), dim3(WM * WN * kWave), lds,
+                       stream, bt);
     return hipGetLastError();
 }
 
@@ -1814,9 +1872,20 @@ int splitk_rt(int M) { return M <= 16 ? 2 : 1; }
 #ifndef MEDUSA_TILE_STORE
 #define MEDUSA_TILE_STORE 1
 #endif
+#ifndef MEDUSA_TILE_SPLIT
+#define MEDUSA_TILE_SPLIT 1
+#endif
+#ifndef MEDUSA_TILE_SPLIT_ROWS
+#define MEDUSA_TILE_SPLIT_ROWS 128
+#endif
 constexpr int kTileRtw = 4;
+constexpr int kBigTile = 256;           // rows and columns of the sliced tiled kernel's tile
 bool tile_store_eligible(medusa_dtype dt, int M, int K) {
     return MEDUSA_TILE_STORE && dt == MEDUSA_BF16 && M >= 384 && K % 64 == 0;
+}
+// The sliced 256 x 256 tiled kernel: bf16 from MEDUSA_TILE_SPLIT_ROWS input rows.
+bool tile_split_eligible(medusa_dtype dt, int M, int K) {
+    return MEDUSA_TILE_SPLIT && dt == MEDUSA_BF16 && M >= MEDUSA_TILE_SPLIT_ROWS && K % 64 == 0;
 }
 
 template <int MT, int RT>
@@ -1865,7 +1934,7 @@ bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
 int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
     if (epi == EPI_STORE && tile_store_eligible(dt, M, K)) return 32 * kTileRtw;
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
-    if (epi == EPI_PARTIAL) return kWavePartialRows;
+    if (epi == EPI_PARTIAL) return tile_split_eligible(dt, M, K) ? kBigTile : kWavePartialRows;
     if (rowstream_eligible(dt, epi, M, K))
         return epi == EPI_ARGMAX || epi == EPI_TYPICAL ? kRsWavesArgmax * 16 * kRsRtwArgmax
                                                        : kRsWavesTops * 16 * kRsRtw;
@@ -1946,11 +2015,12 @@ hipError_t launch_rowstream_t(GemmBatch& bt, hipStream_t stream) {
 // verifies in 334 us instead of 469 (411 with a former kernel that staged the inputs in
 // 512-column slabs), and batched 70B in 323 instead of 378.  256-row blocks need 240
 // VGPRs, one workgroup per CU, and measured 384 us.
-// Greedy verification past 64 rows runs on the tiled kernel: 128 input rows x 256 weight
-// rows per workgroup (2 x 4 waves, two workgroups per CU), the same 256-row tiles as the
-// row-streaming kernel.  Dense 256-node tree 333 -> 319 us, batched 70B 320 -> 313 us,
-// 341 nodes at the 8B shape 1.40 -> 1.37 ms per step; 256 x 256 tiles (16 waves) and
-// 256 x 256 with 8 waves of 256 accumulators did no better overall.
+// Greedy verification past 64 rows runs on the tiled kernel, on the same 256-row weight
+// tiles as the row-streaming kernel.  Up to 128 rows: 128 input rows per workgroup (2 x 4
+// waves, two workgroups per CU).  Above: 256 input rows (4 x 4 waves, one workgroup per
+// CU, LDS double-buffered), which halves the bytes each CU moves per flop: dense 256-node
+// tree 320 -> 242 us, batched 70B 315 -> 233 us; at 128 rows the larger tile was slower
+// (t(128) 940 -> 989 us per step), half of it being padding.
 template <int EPI, int RTW, int PF, int CH, int NWV>
 hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
     if (bt.M <= 16) return launch_rowstream_t<1, EPI, RTW, PF, CH, NWV>(bt, stream);
@@ -1959,7 +2029,9 @@ hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
     // the tiled kernel's weight rows per workgroup (WN * RTW * 16) are the tile size that
     // gemm_rows_per_tile() reports, which sizes the partials and the grid
     static_assert(EPI != EPI_ARGMAX || 4 * 4 * 16 == NWV * 16 * RTW, "argmax tile rows");
-    if (EPI == EPI_ARGMAX) return launch_tile<2, 4, 4, 4, EPI_ARGMAX>(bt, stream);
+    if (EPI == EPI_ARGMAX)
+        return bt.M <= 128 ? launch_tile<2, 4, 4, 4, EPI_ARGMAX>(bt, stream)
+                           : launch_tile<4, 4, 4, 4, EPI_ARGMAX, true>(bt, stream);
     return launch_rowstream_t<8, EPI, RTW, PF, CH, NWV>(bt, stream);
 }
 
@@ -1996,9 +2068,37 @@ size_t cu_partial_lds(int nw, int K, int ks) {
 }
 
 PartialPlan partial_plan(medusa_dtype dt, int M, int K, const int* Ns, int n) {
-    PartialPlan pl{0, 0};
+    PartialPlan pl{0, 0, 0};
     if (dt != MEDUSA_BF16 || M <= 16 || K % kPartialChunk != 0) return pl;
-    if (tile_store_eligible(dt, M, K)) return pl;       // the tiled store GEMM, no slices
+    if (tile_split_eligible(dt, M, K)) {
+        // 256 x 256 tiles, in as many contraction slices as fill the CUs best: minimise the
+        // bytes the busiest CU moves (its rounds of X and W chunk rows) plus the slice sums
+        // written and read back, spread over the CUs
+        long long tiles = 0, outs = 0;
+        for (int i = 0; i < n; ++i) {
+            tiles += (Ns[i] + kBigTile - 1) / kBigTile;
+            outs += (long long)M * Ns[i];
+        }
+        tiles *= (M + kBigTile - 1) / kBigTile;
+        const int chunks = K / 64;
+        double best = 0;
+        int best_ks = 1;
+        for (int ks = 1; ks <= 8 && ks <= chunks; ++ks) {
+            const long long rounds = (tiles * ks + kPlanCus - 1) / kPlanCus;
+            const double main = (double)rounds * ((chunks + ks - 1) / ks) * 2 * kBigTile * 64 * 2;
+            const double fin = ks > 1 ? 2.0 * ks * outs * 4 / kPlanCus : 0;
+            if (ks == 1 || main + fin < best) {
+                best = main + fin;
+                best_ks = ks;
+            }
+        }
+        if (best_ks > 1 || !tile_store_eligible(dt, M, K)) {
+            pl.ksplit = best_ks;
+            pl.tile = 1;
+        }
+        return pl;                                   // one slice: the tiled store GEMM
+    }
+    if (tile_store_eligible(dt, M, K)) return pl;
     long long rows = 0;
     bool rows32 = true;
     for (int i = 0; i < n; ++i) {
@@ -2072,7 +2172,10 @@ hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& bt, hipStream_t
     const PartialPlan pl = partial_plan(dt, bt.M, bt.K, Ns, bt.n_problems);
     if (pl.ksplit != bt.ksplit) return hipErrorInvalidValue;      // the caller sized part_val
     hipError_t e;
-    switch (pl.waves) {
+    if (pl.tile) {
+        static_assert(16 * 4 * 4 == kBigTile, "sliced tile");
+        e = launch_tile<4, 4, 4, 4, EPI_PARTIAL, true>(bt, stream);
+    } else switch (pl.waves) {
     case 2: e = launch_cu_partial<2>(bt, rows, stream); break;
     case 4: e = launch_cu_partial<4>(bt, rows, stream); break;
     case 6: e = launch_cu_partial<6>(bt, rows, stream); break;

@@ -88,6 +88,7 @@ hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& batch, hipStream_t s
 struct PartialPlan {
     int ksplit;     // contraction slices; 0: not applicable
     int waves;      // waves per workgroup of the one-workgroup-per-CU kernel; 0: single-wave kernel
+    int tile;       // 1: the 256 x 256 tiled kernel writes the slices (many input rows)
 };
 PartialPlan partial_plan(medusa_dtype dt, int M, int K, const int* Ns, int n);
 hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& batch, hipStream_t stream);
