@@ -34,6 +34,28 @@ constexpr int kAttnWavesSmall = 4;
 constexpr int kAttnWavesLarge = 8;
 constexpr int kAttnLargeRows = 512;
 constexpr int kKeys = 64;          // keys staged per LDS block
+
+// Butterfly steps over lanes l ^ 16 and l ^ 32 on gfx950's lane-swap instructions (VALU,
+// no trip through the LDS crossbar as a shuffle would take).  permlane16_swap(v, v) leaves
+// rows 0, 0, 2, 2 of v (rows of 16 lanes) in its first result and rows 1, 1, 3, 3 in its
+// second; permlane32_swap(v, v) leaves the low half twice and the high half twice.  Every
+// lane of a pair combines the same two values in the same order.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -233,8 +255,7 @@ __global__ __launch_bounds__(NWV * 64) void attn_partial_kernel(const AttnArgs a
                     p[t * 4 + j] = v;
                     mx = fmaxf(mx, v);
                 }
-            mx = fmaxf(mx, shfl_xor_f(mx, 16));
-            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            mx = max_xor32(max_xor16(mx));
             const float m_new = fmaxf(m_run, mx);
             // a row with every key of the step masked (only in the tree) keeps p = 0
             const float m_use = (TREE && m_new == -INFINITY) ? 0.f : m_new;
@@ -276,8 +297,7 @@ __global__ __launch_bounds__(NWV * 64) void attn_partial_kernel(const AttnArgs a
         if (tree) block(std::true_type{}, kb0);
         else block(std::false_type{}, kb0);
     }
-    l_run += shfl_xor_f(l_run, 16);
-    l_run += shfl_xor_f(l_run, 32);
+    l_run = sum_xor32(sum_xor16(l_run));
     if (!row_ok) return;
     const long long base = ((((long long)b * sh.Hkv + g) * n_slots + slot) * sh.rows + r);
     float* wo = a.ws_o + base * D;
