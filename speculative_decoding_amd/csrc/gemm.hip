@@ -1219,6 +1219,31 @@ __global__ __launch_bounds__(NW * kWave) void gemm_cu_partial_kernel(const GemmB
     }
 }
 
+// Four consecutive elements as fp32, through one 8-byte (bf16) or 16-byte (fp32) access.
+template <typename T> __device__ __forceinline__ void load4(const T* p, float (&v)[4]);
+template <> __device__ __forceinline__ void load4<float>(const float* p, float (&v)[4]) {
+    const floatx4 q = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = q[j];
+}
+template <> __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float (&v)[4]) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(q.x << 16);
+    v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(q.y << 16);
+    v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+}
+template <typename T> __device__ __forceinline__ void store4(T* p, const float (&v)[4]);
+template <> __device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
+    *reinterpret_cast<floatx4*>(p) = floatx4{v[0], v[1], v[2], v[3]};
+}
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float (&v)[4]) {
+    uint2 q;
+    q.x = pack_bf16x2(v[0], v[1]);
+    q.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(p) = q;
+}
+
 // Sum the contraction slices of every (m, n) in slice order and apply the store epilogue:
 // out[m][n] = rnd(silu?(sum + bias[n]) + residual[m][n]).  Four consecutive n per thread.
 template <typename T>
@@ -1272,6 +1297,28 @@ __global__ __launch_bounds__(kThreads) void splitk_finalize_kernel(const GemmBat
         rok = rr >= 0 && rr < bt.res_rows_bound;
     }
     T* out = static_cast<T*>(P.out);
+    T* dst = out + (long long)m * P.ldo + n0;
+    const T* bsrc = bias ? bias + n0 : nullptr;
+    const T* rsrc = rok ? res + rr * P.res_stride + n0 : nullptr;
+    // four whole, aligned elements (every thread of a launch agrees): one vector access each
+    // for the bias, the residual and the output instead of four scalar ones
+    constexpr uintptr_t kVec = 4 * sizeof(T) - 1;
+    const bool vec = n0 + 4 <= N && ((uintptr_t)dst & kVec) == 0 &&
+                     (!bsrc || ((uintptr_t)bsrc & kVec) == 0) && (!rsrc || ((uintptr_t)rsrc & kVec) == 0);
+    if (vec) {
+        float bv[4] = {0.f, 0.f, 0.f, 0.f}, rv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bsrc) load4<T>(bsrc, bv);
+        if (rsrc) load4<T>(rsrc, rv);
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = y[j] + bv[j];
+            if (P.silu) v[j] = silu(v[j]);
+            if (rsrc) v[j] += rv[j];
+        }
+        store4<T>(dst, v);
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = n0 + j;
