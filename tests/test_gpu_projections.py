@@ -5,10 +5,12 @@ In a whole step the output projection is a small correction on top of the embedd
 residual, so a step-level check cannot see it go wrong; here the inputs make every term
 count (one case has a zero residual, so node_hidden is the projection alone).  The shapes
 cover each kernel choice: one workgroup per CU (64 rows, 8B-class sizes), row tiles that
-run across the q/k/v boundary, more than 64 rows (several row blocks), fewer than 64, at
-most 16 (direct store kernel), k/v widths that are not a multiple of 32 (single-wave
-kernel), contraction lengths that are not multiples of 64 (direct store kernel), and 384
-rows or more (tiled store kernel, also with widths that end in a partial tile)."""
+run across the q/k/v boundary, fewer than 64 rows, at most 16 (split-contraction store:
+the row-contiguous form when the contraction is a multiple of 256, the operand-layout
+form otherwise), k/v widths that are not a multiple of 32 (single-wave kernel), 128 rows
+or more (256 x 256 tiles in contraction slices, also with widths that end in a partial
+tile and row counts that end in a partial block), and a contraction that is not a
+multiple of 64 at 200 rows (split-contraction store over several row blocks)."""
 import numpy as np
 import pytest
 
@@ -29,6 +31,9 @@ CASES = {
     "kv_width16": (64, 512, 300, 6, 1, 16),
     "rows512": (512, 512, 300, 4, 1, 64),
     "rows400_ragged": (400, 1024, 500, 6, 1, 80),
+    "rows8": (8, 512, 300, 4, 1, 64),
+    "rows8_h320": (8, 320, 300, 4, 1, 64),
+    "rows200_h544": (200, 544, 300, 4, 1, 64),
 }
 
 
