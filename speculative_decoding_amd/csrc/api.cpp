@@ -24,7 +24,7 @@ bool dtype_ok(medusa_dtype dt) { return dt == MEDUSA_BF16 || dt == MEDUSA_F32; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int n_tiles_for(medusa_dtype dt, int M, int epi, int N, int K) {
-    const int rows = gemm_rows_per_tile(dt, M, epi, K);
+    const int rows = gemm_rows_per_tile(dt, M, epi, K, N);
     return (N + rows - 1) / rows;
 }
 

@@ -741,6 +741,23 @@ constexpr int kWavePartialRows = 64;        // weight rows per single-wave slice
 // 8 x 64 181 (one workgroup per CU; its eight-wave barrier gates every chunk), 16 x 32 176.
 constexpr int kRsWavesArgmax = MEDUSA_RS_WAVES_ARGMAX;
 constexpr int kRsRtwArgmax = MEDUSA_RS_RTW_ARGMAX;
+// A small vocabulary leaves CUs idle with 256-row tiles (32000 rows are 125 tiles for 256
+// CUs): below 65536 rows the argmax and typical paths at up to 64 verified rows take
+// 4 waves of 16 rows, 64-row tiles.  Measured at the 7B shape (vocabulary 32000, 64
+// nodes): 256-row tiles 107.8 us, 128 (4 x 32) 82.4, 128 (8 x 16) 82.9, 64 (2 x 32) 80.1,
+// 64 (4 x 16) 75.9.
+#ifndef MEDUSA_RS_SMALL_VOCAB
+#define MEDUSA_RS_SMALL_VOCAB 65536
+#endif
+#ifndef MEDUSA_RS_WAVES_SMALLV
+#define MEDUSA_RS_WAVES_SMALLV 4
+#endif
+#ifndef MEDUSA_RS_RTW_SMALLV
+#define MEDUSA_RS_RTW_SMALLV 1
+#endif
+constexpr int kRsWavesSmallVocab = MEDUSA_RS_WAVES_SMALLV;
+constexpr int kRsRtwSmallVocab = MEDUSA_RS_RTW_SMALLV;
+bool rs_small_vocab(int M, int N) { return M <= 64 && N < MEDUSA_RS_SMALL_VOCAB; }
 
 template <int MT, int EPI, int RTW, int PF, int CH, int NWV>
 __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmBatch bt) {
@@ -1978,13 +1995,15 @@ hipError_t launch_epi(int epi, GemmBatch& bt, hipStream_t stream) {
 
 bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
 
-int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K) {
+int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K, int N) {
     if (epi == EPI_STORE && tile_store_eligible(dt, M, K)) return 32 * kTileRtw;
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
     if (epi == EPI_PARTIAL) return tile_split_eligible(dt, M, K) ? kBigTile : kWavePartialRows;
-    if (rowstream_eligible(dt, epi, M, K))
-        return epi == EPI_ARGMAX || epi == EPI_TYPICAL ? kRsWavesArgmax * 16 * kRsRtwArgmax
-                                                       : kRsWavesTops * 16 * kRsRtw;
+    if (rowstream_eligible(dt, epi, M, K)) {
+        if (epi == EPI_TOPS) return kRsWavesTops * 16 * kRsRtw;
+        return rs_small_vocab(M, N) ? kRsWavesSmallVocab * 16 * kRsRtwSmallVocab
+                                    : kRsWavesArgmax * 16 * kRsRtwArgmax;
+    }
     int rt;
     if (dt == MEDUSA_BF16)
         rt = epi == EPI_TOPS ? StreamCfg<bf16_t, EPI_TOPS>::RT : StreamCfg<bf16_t, EPI_ARGMAX>::RT;
@@ -2082,9 +2101,26 @@ hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
     return launch_rowstream_t<8, EPI, RTW, PF, CH, NWV>(bt, stream);
 }
 
+// Up to 64 rows over a small vocabulary: 4-wave workgroups (128-row tiles).
+template <int EPI>
+hipError_t launch_rowstream_small(GemmBatch& bt, hipStream_t stream) {
+    constexpr int W = kRsWavesSmallVocab, RT = kRsRtwSmallVocab;
+    if (bt.M <= 16) return launch_rowstream_t<1, EPI, RT, kRsPf, kRsChunk, W>(bt, stream);
+    if (bt.M <= 32) return launch_rowstream_t<2, EPI, RT, kRsPf, kRsChunk, W>(bt, stream);
+    return launch_rowstream_t<4, EPI, RT, kRsPf, kRsChunk, W>(bt, stream);
+}
+
 hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
     if (epi == EPI_TOPS)
         return launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunk, kRsWavesTops>(bt, stream);
+    // the tile size follows each problem's width (gemm_rows_per_tile): one launch needs
+    // them all on the same side
+    int small = 0;
+    for (int p = 0; p < bt.n_problems; ++p) small += rs_small_vocab(bt.M, bt.p[p].N) ? 1 : 0;
+    if (small != 0 && small != bt.n_problems) return hipErrorInvalidValue;
+    if (small)
+        return epi == EPI_TYPICAL ? launch_rowstream_small<EPI_TYPICAL>(bt, stream)
+                                  : launch_rowstream_small<EPI_ARGMAX>(bt, stream);
     if (epi == EPI_TYPICAL)
         return launch_rowstream_m<EPI_TYPICAL, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
     return launch_rowstream_m<EPI_ARGMAX, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);

@@ -74,8 +74,9 @@ struct GemmBatch {
     TypicalEpi typ;           // EPI_TYPICAL only
 };
 
-// Rows of W per workgroup for a given configuration.
-int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K);
+// Rows of W per workgroup (one tile) for a given configuration; N is the problem's width
+// (the argmax and typical tiles at up to 64 rows are smaller for a small vocabulary).
+int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K, int N);
 // Fills KC and launches.  Returns hipSuccess or the launch error.
 hipError_t gemm_launch(medusa_dtype dt, int epi, GemmBatch& batch, hipStream_t stream);
 
