@@ -1,16 +1,24 @@
-// Skinny GEMM for gfx950: Y[m, n] = sum_k X[m, k] W[n, k] with few rows m (1..64 per
-// block) and many weight rows n, as in the Medusa heads (one hidden vector per head), the
-// verifier's projections (one row per tree node) and the lm_head over all tree nodes.
+// GEMMs of the decode step on gfx950: Y[m, n] = sum_k X[m, k] W[n, k] with W row-major
+// [n, k] (the nn.Linear layout), fp32 accumulation and fused epilogues (bias/SiLU/residual
+// store, per-tile top-s, per-tile argmax, typical-acceptance sums, fp32 slice sums).
 //
-// Design.  The weight matrix is the only large operand, so every workgroup streams its
-// own slice of W rows from HBM exactly once, straight into MFMA operand registers: lane l
-// of a wave reads 16 contiguous bytes of row (l % 16) at contraction offset 8*(l/16), so
-// one load instruction covers 16 rows x 64 contiguous bytes and four unrolled k-steps
-// cover 256 contiguous bytes per row.  The few X rows are staged through LDS in
-// contraction chunks and re-read from there by all four waves.  The contraction runs on
-// MFMA (16x16x32 bf16, or 16x16x4 fp32) with fp32 accumulation; at one row per head this
-// wastes most of the matrix unit, which costs nothing because the kernel is bound by HBM.
-// Epilogues are fused: bias/SiLU/residual store, per-tile top-s, or per-tile argmax.
+// The weight matrix is the large operand, and a CU's vector memory path moves only so many
+// bytes per second, so each kernel family is shaped by the bytes the busiest CU moves:
+//   gemv_bf16_kernel          1-2 input rows (the heads at batch 1-2): whole rows of W per
+//                             wave, 1 KiB per load instruction, dot products on the VALU;
+//   gemm_rowstream_kernel     up to 64 rows (lm_head over the tree, heads from batch 3):
+//                             8 rows x 128 B per load instruction through a wave-private
+//                             LDS transpose into MFMA operands, input chunk shared in LDS;
+//   gemm_cu_partial_kernel    the verifier's projections at 17-127 rows: one workgroup per
+//                             CU, contraction slices summed by splitk_finalize_kernel;
+//   gemm_tile_kernel          from 128 rows (argmax: above 64): 128 x 128, 128 x 256 or
+//                             256 x 256 MFMA tiles, contraction slices for the projections;
+//   gemm_splitk_rows_kernel   few rows with a store epilogue (the heads' feed-forward block
+//                             from batch 3): the four waves split the contraction;
+//   gemm_kernel, gemm_splitk_store_kernel, gemm_wave_partial_kernel   the shapes the above
+//                             do not take (fp32, contractions or widths off their multiples).
+// The MEDUSA_* macros below are compile-time tuning parameters; their defaults are the
+// measured best on MI355X.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -563,6 +571,10 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBa
     }
 }
 
+// Generic MFMA kernel (fp32, and bf16 shapes the specialised kernels do not take): each
+// wave streams its RT*16 weight rows straight into MFMA operand registers (lane l reads 16
+// bytes of row l % 16 at contraction offset 8*(l/16), UN k-steps unrolled); the few X rows
+// are staged through LDS in contraction chunks and shared by the four waves.
 template <typename T, int MT, int RT, int UN, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
     using E = Elem<T>;
