@@ -572,8 +572,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& P, const GemmBa
 }
 
 // Generic MFMA kernel (fp32, and bf16 shapes the specialised kernels do not take): each
-// wave streams its RT*16 weight rows straight into MFMA operand registers (lane l reads 16
-// bytes of row l % 16 at contraction offset 8*(l/16), UN k-steps unrolled); the few X rows
+// wave streams its RT*16 weight rows straight into MFMA operand registers (lane l reads 8
+// elements of row l % 16 at contraction offset 8*(l/16), UN k-steps unrolled); the few X rows
 // are staged through LDS in contraction chunks and shared by the four waves.
 template <typename T, int MT, int RT, int UN, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmBatch bt) {
