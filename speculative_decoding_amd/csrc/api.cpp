@@ -554,13 +554,25 @@ medusa_status medusa_advance(const medusa_tree_plan* plan, medusa_dtype dt, int 
 
 namespace {
 
-// Contraction slices for the verifier's two projections (0: direct store kernel).
-int qkv_ksplit(medusa_dtype dt, int M, int H, int Hq, int Hkv, int d) {
+// Plans of the verifier's two projections (ksplit 0: direct store kernel).
+PartialPlan qkv_plan(medusa_dtype dt, int M, int H, int Hq, int Hkv, int d) {
     const int Ns[3] = {Hq * d, Hkv * d, Hkv * d};
-    return partial_plan(dt, M, H, Ns, 3).ksplit;
+    return partial_plan(dt, M, H, Ns, 3);
+}
+PartialPlan out_plan(medusa_dtype dt, int M, int H, int Hq, int d) {
+    return partial_plan(dt, M, Hq * d, &H, 1);
+}
+int qkv_ksplit(medusa_dtype dt, int M, int H, int Hq, int Hkv, int d) {
+    return qkv_plan(dt, M, H, Hq, Hkv, d).ksplit;
 }
 int out_ksplit(medusa_dtype dt, int M, int H, int Hq, int d) {
-    return partial_plan(dt, M, Hq * d, &H, 1).ksplit;
+    return out_plan(dt, M, H, Hq, d).ksplit;
+}
+// Weight-row tiles of one projection problem of width N.
+int proxy_tiles(medusa_dtype dt, const PartialPlan& pl, int M, int N, int K) {
+    if (pl.ksplit == 0) return n_tiles_for(dt, M, EPI_STORE, N, K);
+    const int r = partial_tile_rows(pl);
+    return (N + r - 1) / r;
 }
 
 }  // namespace
@@ -583,11 +595,11 @@ medusa_status medusa_proxy_qkv(medusa_dtype dt, int M, int H, int V, int Hq, int
         return MEDUSA_ERR_SHAPE;
     if (!aligned16(embed) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv))
         return MEDUSA_ERR_SHAPE;
-    const int ks = qkv_ksplit(dt, M, H, Hq, Hkv, d);
+    const PartialPlan pl = qkv_plan(dt, M, H, Hq, Hkv, d);
+    const int ks = pl.ksplit;
     if (!ws || ws_bytes < medusa_proxy_workspace(dt, M, H, Hq, Hkv, d)) return MEDUSA_ERR_WORKSPACE;
     medusa_status st = medusa_internal_device_check();
     if (st != MEDUSA_OK) return st;
-    const int epi = ks > 0 ? EPI_PARTIAL : EPI_STORE;
     GemmBatch g{};
     g.n_problems = 3;
     g.M = M;
@@ -607,7 +619,7 @@ medusa_status medusa_proxy_qkv(medusa_dtype dt, int M, int H, int V, int Hq, int
         p.x_stride = H;
         p.N = Nn[i];
         p.tile_begin = tiles;
-        p.n_tiles = n_tiles_for(dt, M, epi, Nn[i], H);
+        p.n_tiles = proxy_tiles(dt, pl, M, Nn[i], H);
         tiles += p.n_tiles;
         p.out = O[i];
         p.ldo = Nn[i];
@@ -633,12 +645,12 @@ medusa_status medusa_proxy_out(medusa_dtype dt, int M, int H, int V, int Hq, int
     if (M < 1 || H < 16 || H % 16 != 0 || V < 1 || Hq < 1 || d < 1 || (Hq * d) % 32 != 0)
         return MEDUSA_ERR_SHAPE;
     if (!aligned16(embed) || !aligned16(o) || !aligned16(wo)) return MEDUSA_ERR_SHAPE;
-    const int ks = out_ksplit(dt, M, H, Hq, d);
+    const PartialPlan pl = out_plan(dt, M, H, Hq, d);
+    const int ks = pl.ksplit;
     const size_t need = align256((size_t)(ks > 0 ? ks : 0) * M * (size_t)H * sizeof(float)) + 256;
     if (!ws || ws_bytes < need) return MEDUSA_ERR_WORKSPACE;
     medusa_status st = medusa_internal_device_check();
     if (st != MEDUSA_OK) return st;
-    const int epi = ks > 0 ? EPI_PARTIAL : EPI_STORE;
     GemmBatch g{};
     g.n_problems = 1;
     g.M = M;
@@ -651,7 +663,7 @@ medusa_status medusa_proxy_out(medusa_dtype dt, int M, int H, int V, int Hq, int
     p.x_stride = (long long)Hq * d;
     p.N = H;
     p.tile_begin = 0;
-    p.n_tiles = n_tiles_for(dt, M, epi, H, Hq * d);
+    p.n_tiles = proxy_tiles(dt, pl, M, H, Hq * d);
     p.out = node_hidden;
     p.ldo = H;
     p.res = embed;

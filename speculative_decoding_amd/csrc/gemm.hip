@@ -1952,14 +1952,15 @@ int splitk_rt(int M) { return M <= 16 ? 2 : 1; }
 #define MEDUSA_TILE_SPLIT 1
 #endif
 #ifndef MEDUSA_TILE_SPLIT_ROWS
-#define MEDUSA_TILE_SPLIT_ROWS 128
+#define MEDUSA_TILE_SPLIT_ROWS 17
 #endif
 constexpr int kTileRtw = 4;
 constexpr int kBigTile = 256;           // rows and columns of the sliced tiled kernel's tile
 bool tile_store_eligible(medusa_dtype dt, int M, int K) {
     return MEDUSA_TILE_STORE && dt == MEDUSA_BF16 && M >= 384 && K % 64 == 0;
 }
-// The sliced 256 x 256 tiled kernel: bf16 from MEDUSA_TILE_SPLIT_ROWS input rows.
+// The sliced 256 x 256 tiled kernel may run (bf16 from MEDUSA_TILE_SPLIT_ROWS input rows);
+// partial_plan() decides whether it does.
 bool tile_split_eligible(medusa_dtype dt, int M, int K) {
     return MEDUSA_TILE_SPLIT && dt == MEDUSA_BF16 && M >= MEDUSA_TILE_SPLIT_ROWS && K % 64 == 0;
 }
@@ -2010,7 +2011,7 @@ bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K);
 int gemm_rows_per_tile(medusa_dtype dt, int M, int epi, int K, int N) {
     if (epi == EPI_STORE && tile_store_eligible(dt, M, K)) return 32 * kTileRtw;
     if (epi == EPI_STORE) return 16 * splitk_rt(M);
-    if (epi == EPI_PARTIAL) return tile_split_eligible(dt, M, K) ? kBigTile : kWavePartialRows;
+    if (epi == EPI_PARTIAL) return kWavePartialRows;     // the tiled kernel: partial_tile_rows()
     if (rowstream_eligible(dt, epi, M, K)) {
         if (epi == EPI_TOPS) return kRsWavesTops * 16 * kRsRtw;
         return rs_small_vocab(M, N) ? kRsWavesSmallVocab * 16 * kRsRtwSmallVocab
@@ -2165,46 +2166,18 @@ size_t cu_partial_lds(int nw, int K, int ks) {
 PartialPlan partial_plan(medusa_dtype dt, int M, int K, const int* Ns, int n) {
     PartialPlan pl{0, 0, 0};
     if (dt != MEDUSA_BF16 || M <= 16 || K % kPartialChunk != 0) return pl;
-    if (tile_split_eligible(dt, M, K)) {
-        // 256 x 256 tiles, in as many contraction slices as fill the CUs best: minimise the
-        // bytes the busiest CU moves (its rounds of X and W chunk rows) plus the slice sums
-        // written and read back, spread over the CUs
-        long long tiles = 0, outs = 0;
-        for (int i = 0; i < n; ++i) {
-            tiles += (Ns[i] + kBigTile - 1) / kBigTile;
-            outs += (long long)M * Ns[i];
-        }
-        tiles *= (M + kBigTile - 1) / kBigTile;
-        const int chunks = K / 64;
-        double best = 0;
-        int best_ks = 1;
-        for (int ks = 1; ks <= 8 && ks <= chunks; ++ks) {
-            const long long rounds = (tiles * ks + kPlanCus - 1) / kPlanCus;
-            const double main = (double)rounds * ((chunks + ks - 1) / ks) * 2 * kBigTile * 64 * 2;
-            const double fin = ks > 1 ? 2.0 * ks * outs * 4 / kPlanCus : 0;
-            if (ks == 1 || main + fin < best) {
-                best = main + fin;
-                best_ks = ks;
-            }
-        }
-        if (best_ks > 1 || !tile_store_eligible(dt, M, K)) {
-            pl.ksplit = best_ks;
-            pl.tile = 1;
-        }
-        return pl;                                   // one slice: the tiled store GEMM
-    }
-    if (tile_store_eligible(dt, M, K)) return pl;
     long long rows = 0;
     bool rows32 = true;
     for (int i = 0; i < n; ++i) {
         rows += Ns[i];
         rows32 = rows32 && Ns[i] % (16 * kCuRt) == 0;
     }
-    const int n_mb = (M + 63) / 64;
+    // Both candidates are priced in the bytes the busiest CU moves: its rounds of weight and
+    // input rows, its slice sums, and its share of the finalize pass.
+    double best = -1;
     if (rows32 && K % kCuChunk == 0) {
-        // one workgroup per CU: minimise the bytes the busiest CU moves (weights, staged
-        // input slice, slice sums) plus its share of the finalize pass
-        double best = 0;
+        // one workgroup per CU, 64-row input blocks
+        const int n_mb = (M + 63) / 64;
         static const int kWavesOpt[] = {2, 4, 6, 8};
         static const int kSplitOpt[] = {1, 2, 4, 8, 16};
         for (int nw : kWavesOpt)
@@ -2217,21 +2190,45 @@ PartialPlan partial_plan(medusa_dtype dt, int M, int K, const int* Ns, int n) {
                 const double per_wg = R * slice * 2 + 64 * slice * 2 + (ks > 1 ? R * 64 * 4 : 0);
                 const double fin = ks > 1 ? (double)ks * M * rows * 4 / kPlanCus : 0;
                 const double cost = rounds * per_wg + fin;
-                if (pl.waves == 0 || cost < best) {
+                if (best < 0 || cost < best) {
                     best = cost;
-                    pl.waves = nw;
-                    pl.ksplit = ks;
+                    pl = PartialPlan{ks, nw, 0};
                 }
             }
-        if (pl.waves) return pl;
     }
+    if (tile_split_eligible(dt, M, K)) {
+        // 256 x 256 tiles (input rows past M cost no bandwidth: they read nothing new) in
+        // as many contraction slices as fill the CUs best
+        long long tiles = 0;
+        for (int i = 0; i < n; ++i) tiles += (Ns[i] + kBigTile - 1) / kBigTile;
+        tiles *= (M + kBigTile - 1) / kBigTile;
+        const int chunks = K / 64;
+        const double mv = std::min(M, kBigTile);
+        for (int ks = 1; ks <= 16 && ks <= chunks; ++ks) {
+            const long long rounds = (tiles * ks + kPlanCus - 1) / kPlanCus;
+            const double slice = (double)((chunks + ks - 1) / ks) * 64;
+            const double per_wg = (kBigTile + mv) * slice * 2;
+            // one slice from 384 rows is the unsliced tiled store: no slice sums
+            const bool sums = ks > 1 || !tile_store_eligible(dt, M, K);
+            const double fin = sums ? 2.0 * ks * M * rows * 4 / kPlanCus : 0;
+            const double cost = rounds * per_wg + fin;
+            if (best < 0 || cost < best) {
+                best = cost;
+                pl = sums ? PartialPlan{ks, 0, 1} : PartialPlan{0, 0, 0};
+            }
+        }
+    }
+    if (best >= 0) return pl;
     // per-problem 64-row tiles on the single-wave kernel
+    const int n_mb = (M + 63) / 64;
     long long tiles = 0;
     for (int i = 0; i < n; ++i) tiles += (Ns[i] + 63) / 64;
     const long long want = (MEDUSA_KSPLIT_WG + tiles * n_mb - 1) / (tiles * n_mb);
     pl.ksplit = (int)std::max(1LL, std::min(want, (long long)std::min(16, K / kPartialChunk)));
     return pl;
 }
+
+int partial_tile_rows(const PartialPlan& pl) { return pl.tile ? kBigTile : kWavePartialRows; }
 
 template <int MT>
 hipError_t launch_wave_partial(GemmBatch& bt, hipStream_t stream) {

@@ -92,6 +92,8 @@ struct PartialPlan {
     int tile;       // 1: the 256 x 256 tiled kernel writes the slices (many input rows)
 };
 PartialPlan partial_plan(medusa_dtype dt, int M, int K, const int* Ns, int n);
+// Weight rows per tile of a plan's slice kernel (problem tiles: ceil(N / this)).
+int partial_tile_rows(const PartialPlan& pl);
 hipError_t gemm_store_partial_launch(medusa_dtype dt, GemmBatch& batch, hipStream_t stream);
 
 // ------------------------------------------------------------------ top-s merge
