@@ -441,7 +441,9 @@ AttnShape attn_shape(int B, int N, int Hq, int Hkv, int d, int Lcap) {
     const int max_splits = Lcap > 0 ? (Lcap + kKeys - 1) / kKeys : 1;
     int splits = Lcap / (2 * s.rows);
     const int base = B * Hkv * s.n_qblocks;
-    const int fill_blocks = 2048 / s.waves;           // about 2048 waves in flight
+    // about 1024 waves in flight: with 2048 (twice the splits) the 8B tree took 22.6 + 8.9
+    // us, against 22.2 + 7.8 here (7B shape 15.7 + 8.9 against 13.2 + 8.1)
+    const int fill_blocks = 1024 / s.waves;
     const int fill = (fill_blocks + base - 1) / base;
     if (splits < fill) splits = fill;
     if (splits < 1) splits = 1;
