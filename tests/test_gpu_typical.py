@@ -112,19 +112,22 @@ def test_typical_run_twice_bitwise(dev):
 
 
 @pytest.mark.slow
-def test_typical_8b(dev):
+@pytest.mark.parametrize("cfg", ["8b", "mid"])
+def test_typical_full_size(dev, cfg):
+    """The benchmark shapes: 8B (256-row vocabulary tiles) and 7B (vocabulary 32000,
+    64-row tiles)."""
     import os
     import torch
     from tests.gpu_util import PLANTS
-    if not os.path.exists(os.path.join(PLANTS, "8b_s0.json")):
-        pytest.skip("no stored plant for 8b seed 0")
-    say("[typical 8b seed 0] generating")
-    inp = planted("8b", 0)
+    if not os.path.exists(os.path.join(PLANTS, f"{cfg}_s0.json")):
+        pytest.skip(f"no stored plant for {cfg} seed 0")
+    say(f"[typical {cfg} seed 0] generating")
+    inp = planted(cfg, 0)
     plan = oracle_plan(inp)
-    say("[typical 8b seed 0] gpu step")
+    say(f"[typical {cfg} seed 0] gpu step")
     step, got = run_gpu(inp, dev, keep_logits=False, keep_u=False, typical=(0.5, 0.09, 0.3))
     del step
     torch.cuda.empty_cache()
-    say("[typical 8b seed 0] oracle step")
+    say(f"[typical {cfg} seed 0] oracle step")
     ref = oracle.step(inp, plan)
     _check_typical(inp, got, ref, plan, 0.5, 0.09, 0.3)
