@@ -59,3 +59,24 @@ def test_batch64_step(dev):
     _, got = run_gpu(inp, dev, keep_logits=True)
     compare_step(inp, got, ref, plan=plan)
     say(f"    accept {got['accept_len'].tolist()}")
+
+
+@pytest.mark.parametrize("V", [65535, 65536])
+def test_vocabulary_tile_boundary(dev, V):
+    """Verification at up to 64 rows takes 64-row vocabulary tiles below 65536 rows and
+    256-row tiles from there: a whole step on each side of the switch (the small shape with
+    its vocabulary widened), unplanted, so accept results follow the device's decisions."""
+    import dataclasses
+    from synth import get_config
+    say(f"[limits: vocabulary {V}]")
+    cfg = dataclasses.replace(get_config("small"), name=f"small_v{V}", V=V)
+    inp = make_inputs(cfg, 0)
+    plan = oracle_plan(inp)
+    ref = oracle.step(inp, plan)
+    r = np.sort(ref.root_logits[0])[-2:]
+    assert r[1] - r[0] >= 1e-4, "the draw has a near-tie at the root"
+    for k in range(cfg.K):
+        v = np.sort(ref.head_logits[0, k])[::-1][: cfg.s[k] + 1]
+        assert np.min(v[:-1] - v[1:]) >= 1e-4, "the draw has a near-tie in a head's top-k"
+    _, got = run_gpu(inp, dev, keep_logits=True)
+    compare_step(inp, got, ref, plan=plan)
