@@ -566,3 +566,177 @@ def test_root_only_decode_loop_is_greedy_decoding():
     for b in range(inp.cfg.B):
         g, _, _ = oracle.greedy_decode(inp, b, int(root0[b]), 5)
         assert streams[b].tolist() == g.tolist()
+
+
+# ------------------------------------------------------------------ tree plan (oracle only)
+#
+# The glossary page "Medusa Heads", section "Attention arborescente et acceptation":
+# candidates are the Cartesian product of the heads' best ranks (2 x 3 -> six
+# continuations), arranged as a tree with shared prefixes, and a sparse tree keeps the
+# most accurate combinations.  These pins use the oracle alone; no library is loaded.
+
+def _popcount(x: int) -> int:
+    return bin(int(x)).count("1")
+
+
+def _downsets_of(widths):
+    """Every prefix-closed set of rank tuples of the Cartesian tree with these
+    per-depth widths (the root excluded), enumerated by choosing, for every child of
+    a chosen node, whether it and which of its own descendants are kept."""
+    def below(prefix):
+        d = len(prefix)
+        if d == len(widths):
+            return [[]]
+        per_child = []
+        for r in range(widths[d]):
+            t = prefix + (r,)
+            per_child.append([[]] + [[t] + rest for rest in below(t)])
+        return [[x for part in combo for x in part] for combo in itertools.product(*per_child)]
+    return below(())
+
+
+def _expected_accept_by_enumeration(paths, acc, widths):
+    """E[accepted candidates] with independent heads: head k is right at rank i with
+    probability acc[k][i] and at no kept rank otherwise; the walk accepts depth d when
+    the tuple of the first d outcomes is in the tree.  Every joint outcome is listed."""
+    present = set(tuple(p) for p in paths)
+    outcomes = []
+    for k, w in enumerate(widths):
+        o = [(i, float(acc[k][i])) for i in range(w)]
+        o.append((-1, 1.0 - sum(p for _, p in o)))
+        outcomes.append(o)
+    e = 0.0
+    for joint in itertools.product(*outcomes):
+        p = 1.0
+        for _, pk in joint:
+            p *= pk
+        a = 0
+        for d in range(1, len(widths) + 1):
+            t = tuple(r for r, _ in joint[:d])
+            if -1 in t or t not in present:
+                break
+            a = d
+        e += p * a
+    return e
+
+
+@pytest.mark.parametrize("widths,nodes,leaves", [((2, 3), 9, 6), ((3, 4, 4, 4), 256, 192),
+                                                 ((4, 4, 4, 4), 341, 256), ((5,), 6, 5),
+                                                 ((1, 1, 1, 1, 1), 6, 1), ((2, 1, 3), 11, 6)])
+def test_plan_full_node_counts(widths, nodes, leaves):
+    """Closed forms: a full Cartesian tree has 1 + sum_d prod_{k<=d} s_k nodes and
+    prod_k s_k leaves; the page's 2 x 3 example has six candidate continuations."""
+    plan = oracle.plan_full(widths)
+    assert plan.n_nodes == nodes
+    assert len(plan.leaves()) == leaves
+    assert plan.max_depth == len(widths)
+    assert plan.mask_words == (nodes + 63) // 64
+    per_depth = np.bincount(plan.depth, minlength=len(widths) + 1).tolist()
+    assert per_depth == [1] + [int(np.prod(widths[:d])) for d in range(1, len(widths) + 1)]
+
+
+def test_plan_full_page_example_written_out():
+    """The 2 x 3 tree, breadth first, written out by hand: the root, head 1's two
+    candidates, then head 2's three candidates under each of them."""
+    plan = oracle.plan_full((2, 3))
+    assert plan.paths == [(), (0,), (1,), (0, 0), (0, 1), (0, 2), (1, 0), (1, 1), (1, 2)]
+    assert plan.parent.tolist() == [-1, 0, 0, 1, 1, 1, 2, 2, 2]
+    assert plan.depth.tolist() == [0, 1, 1, 2, 2, 2, 2, 2, 2]
+    assert plan.rank.tolist() == [-1, 0, 1, 0, 1, 2, 0, 1, 2]
+    # node i sees the root, its parent (for depth 2) and itself
+    want = [0b1, 0b11, 0b101, 0b1011, 0b10011, 0b100011, 0b1000101, 0b10000101, 0b100000101]
+    assert plan.mask_bits()[:, 0].tolist() == want
+    assert plan.leaves() == [3, 4, 5, 6, 7, 8]
+
+
+@pytest.mark.parametrize("widths", [(2, 3), (3, 4, 4, 4), (4, 4, 4, 4), (3, 2, 2, 2, 2, 2, 2)])
+def test_plan_mask_bits_follow_parent_chain(widths):
+    """Row i of the mask has exactly the nodes on the parent chain from i up to the
+    root: popcount = depth + 1, bit i set, and bit j set only for j <= i.  Trees past 64
+    nodes check the split over 64-bit words."""
+    plan = oracle.plan_full(widths)
+    bits = plan.mask_bits()
+    assert bits.shape == (plan.n_nodes, (plan.n_nodes + 63) // 64)
+    for i in range(plan.n_nodes):
+        chain = set()
+        j = i
+        while j >= 0:
+            chain.add(j)
+            j = int(plan.parent[j])
+        got = {64 * w + b for w in range(bits.shape[1]) for b in range(64)
+               if (int(bits[i, w]) >> b) & 1}
+        assert got == chain, i
+        assert sum(_popcount(x) for x in bits[i]) == plan.depth[i] + 1
+        assert max(got) == i
+
+
+def test_plan_from_accuracy_ties_written_out():
+    """Ties broken by depth (shallower first), then by the rank tuple: with accuracies
+    that are powers of two, the scores tie exactly.  Scores: (0)=1/2, (1)=1/4, (0,0)=1/4,
+    (0,1)=1/8, (1,0)=1/8, (1,1)=1/16."""
+    acc = np.array([[0.5, 0.25], [0.5, 0.25]])
+    want = {
+        1: [()],
+        2: [(), (0,)],
+        3: [(), (0,), (1,)],                               # (1) before (0,0): shallower
+        4: [(), (0,), (1,), (0, 0)],
+        5: [(), (0,), (1,), (0, 0), (0, 1)],               # (0,1) before (1,0): tuple order
+        6: [(), (0,), (1,), (0, 0), (0, 1), (1, 0)],
+        7: [(), (0,), (1,), (0, 0), (0, 1), (1, 0), (1, 1)],
+    }
+    for n, paths in want.items():
+        assert oracle.plan_from_accuracy(acc, (2, 2), n).paths == paths, n
+    with pytest.raises(ValueError):
+        oracle.plan_from_accuracy(acc, (2, 2), 8)
+
+
+def _check_prefix_closed_contiguous(plan):
+    present = set(plan.paths)
+    for t in plan.paths[1:]:
+        assert t[:-1] in present, t
+        if t[-1] > 0:
+            assert t[:-1] + (t[-1] - 1,) in present, t     # sibling ranks are contiguous
+    # breadth-first order: depth ascending, then rank tuple ascending
+    assert plan.paths == sorted(plan.paths, key=lambda t: (len(t), t))
+
+
+@pytest.mark.parametrize("widths,seed", [((3, 2, 2), 4), ((2, 3, 2), 5), ((2, 2, 2, 1), 6)])
+def test_plan_from_accuracy_is_best_prefix_closed_tree(widths, seed):
+    """Brute force over every prefix-closed node set of a small Cartesian tree: at every
+    size, the most-accurate selection has the largest expected accepted length (each set's
+    E[a] found by listing every joint outcome of the heads), and it is prefix-closed with
+    contiguous sibling ranks."""
+    rng = np.random.default_rng(seed)
+    acc = np.zeros((len(widths), max(widths)))
+    for k, w in enumerate(widths):
+        raw = np.sort(rng.uniform(0.02, 0.5, size=w))[::-1]
+        acc[k, :w] = raw * (0.9 / raw.sum())                # a miss keeps some mass
+    best = {}
+    for ds in _downsets_of(widths):
+        e = _expected_accept_by_enumeration(ds, acc, widths)
+        best[len(ds)] = max(best.get(len(ds), -1.0), e)
+    n_cands = len(oracle.candidate_tuples(widths))
+    assert sorted(best) == list(range(n_cands + 1))
+    for n_paths, e in best.items():
+        plan = oracle.plan_from_accuracy(acc, widths, n_paths + 1)
+        assert plan.n_nodes == n_paths + 1
+        _check_prefix_closed_contiguous(plan)
+        got = _expected_accept_by_enumeration(plan.paths[1:], acc, widths)
+        assert abs(got - e) < 1e-12, (n_paths, got, e)
+
+
+def test_plan_from_accuracy_on_the_workload_tables():
+    """The benchmark's 64-node sparse trees: prefix-closed, contiguous, at most one node
+    per rank tuple, depth bounded by the heads, and the whole Cartesian tree when every
+    candidate is asked for."""
+    from synth import get_config
+    for name in ("mid", "8b", "batched70b"):
+        cfg = get_config(name)
+        acc = accuracy_table(cfg, 0)
+        plan = oracle.plan_from_accuracy(acc, cfg.tree_s, cfg.n_nodes)
+        assert plan.n_nodes == cfg.n_nodes
+        _check_prefix_closed_contiguous(plan)
+        assert plan.max_depth <= len(cfg.tree_s)
+        assert all(t[d] < cfg.tree_s[d] for t in plan.paths for d in range(len(t)))
+    full = oracle.plan_from_accuracy(accuracy_table(get_config("8b"), 0), (3, 2, 2), 1 + 3 + 6 + 12)
+    assert full.paths == oracle.plan_full((3, 2, 2)).paths
