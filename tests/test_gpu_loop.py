@@ -89,9 +89,8 @@ def test_advance_matches_oracle(dev, cfg, seed):
         assert torch.equal(w["h"][b], nh[b, path[a]])
         # and they equal the oracle's rows within the activation tolerance
         close(f"seq {b} appended k", kc[b, L: L + a + 1].float().cpu().numpy(),
-              oracle.as_f64(nxt.k_cache[b, L: L + a + 1], inp.dtype), row_scale=True)
-        close(f"seq {b} next h", w["h"][b].float().cpu().numpy(), oracle.as_f64(nxt.h[b], inp.dtype),
-              row_scale=True)
+              oracle.as_f64(nxt.k_cache[b, L: L + a + 1], inp.dtype))
+        close(f"seq {b} next h", w["h"][b].float().cpu().numpy(), oracle.as_f64(nxt.h[b], inp.dtype))
 
 
 def test_advance_overflow_changes_nothing(dev):

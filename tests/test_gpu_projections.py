@@ -96,7 +96,7 @@ def test_projections(dev, name, residual):
         outs.append([t.clone() for t in (q, k, v, nh)])
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name}: second call differs"
-    close(f"{name} q", _host(q).reshape(q_ref.shape), q_ref, row_scale=True)
-    close(f"{name} k", _host(k).reshape(k_ref.shape), k_ref, row_scale=True)
-    close(f"{name} v", _host(v).reshape(v_ref.shape), v_ref, row_scale=True)
-    close(f"{name} node_hidden", _host(nh).reshape(nh_ref.shape), nh_ref, row_scale=True)
+    close(f"{name} q", _host(q).reshape(q_ref.shape), q_ref)
+    close(f"{name} k", _host(k).reshape(k_ref.shape), k_ref)
+    close(f"{name} v", _host(v).reshape(v_ref.shape), v_ref)
+    close(f"{name} node_hidden", _host(nh).reshape(nh_ref.shape), nh_ref)

@@ -10,24 +10,29 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import close, exact, oracle_plan, planted, run_gpu, say
+from tests.gpu_util import close, close_verify_logits, exact, oracle_plan, planted, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
 PROB_RTOL = 2e-2
 PROB_ATOL = 1e-30
 
-# (config, seed, temperature, epsilon, delta); configurations cover the fp32 kernel (tiny),
-# the row-streaming kernel (up to 64 rows), the slab kernel (more than 64 rows), several
-# sequences, flat (T = 1) and sharp (small T) distributions
+# (config, seed, temperature, epsilon, delta, sure); configurations cover the fp32 kernel
+# (tiny), the row-streaming kernel with one 64-row block (small), with 128-row blocks past
+# 64 verified rows (small_dense: 170 rows over two sequences; small_n341), several sequences
+# (small_batched, small_dense), flat (T = 1) and sharp (small T) distributions.  Where
+# ``sure`` is set the oracle puts no candidate within tolerance of its threshold (checked
+# in the test), so the accept results must equal the oracle's.
 CASES = [
-    ("tiny", 0, 1.0, 0.3, 0.09),
-    ("tiny", 2, 0.2, 0.09, 0.3),
-    ("small", 0, 1.0, 0.09, 0.3),
-    ("small", 1, 0.05, 0.09, 0.3),
-    ("small_batched", 0, 0.5, 0.2, 0.5),
-    ("small_dense", 0, 1.0, 0.09, 0.3),
-    ("small_n341", 0, 0.7, 0.05, 0.5),
+    ("tiny", 0, 1.0, 0.3, 0.09, True),
+    ("tiny", 2, 0.2, 0.09, 0.3, True),
+    ("small", 0, 1.0, 0.09, 0.3, True),
+    ("small", 1, 0.05, 0.09, 0.3, True),
+    ("small_batched", 0, 0.5, 0.2, 0.5, True),
+    ("small_dense", 0, 1.0, 0.09, 0.3, False),
+    ("small_dense", 0, 0.7, 0.05, 0.5, True),
+    ("small_n341", 0, 0.7, 0.05, 0.5, False),
+    ("small_n341", 0, 0.5, 0.09, 0.3, True),
 ]
 
 
@@ -40,7 +45,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _check_typical(inp, got, ref, plan, T, eps, delta):
+def _check_typical(inp, got, ref, plan, T, eps, delta, sure=False):
     a, nodes, toks, prob, tau = oracle.typical_accept(plan, ref.tokens, ref.logits,
                                                       ref.node_argmax, T, eps, delta)
     exact("root_ids", got["root_ids"], ref.root)
@@ -64,6 +69,8 @@ def _check_typical(inp, got, ref, plan, T, eps, delta):
             par = int(plan.parent[i])
             if abs(prob[b, i] - tau[b, par]) <= PROB_RTOL * max(prob[b, i], tau[b, par]):
                 close_calls += 1
+    if sure:
+        assert close_calls == 0, f"{close_calls} oracle decisions sit within tolerance"
     if close_calls == 0:
         exact("accept_len", got["accept_len"], a)
         exact("accept_nodes", got["accept_nodes"], nodes)
@@ -72,15 +79,16 @@ def _check_typical(inp, got, ref, plan, T, eps, delta):
         f"{close_calls} decisions within tolerance of the threshold")
 
 
-@pytest.mark.parametrize("cfg,seed,T,eps,delta", CASES)
-def test_typical_step(dev, cfg, seed, T, eps, delta):
+@pytest.mark.parametrize("cfg,seed,T,eps,delta,sure", CASES)
+def test_typical_step(dev, cfg, seed, T, eps, delta, sure):
     say(f"[typical {cfg} seed {seed} T={T} eps={eps} delta={delta}]")
     inp = planted(cfg, seed)
     plan = oracle_plan(inp)
     ref = oracle.step(inp, plan)
     _, got = run_gpu(inp, dev, typical=(T, eps, delta))
-    _check_typical(inp, got, ref, plan, T, eps, delta)
-    close("verify_logits", got["verify_logits"], ref.logits, row_scale=True)
+    _check_typical(inp, got, ref, plan, T, eps, delta, sure)
+    close_verify_logits("verify_logits", got["verify_logits"], ref.logits, got["node_hidden"],
+                        ref.node_hidden, inp.w_lm, inp.dtype)
 
 
 @pytest.mark.parametrize("cfg,seed", [("tiny", 1), ("small", 0), ("small_batched", 1),
