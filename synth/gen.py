@@ -233,6 +233,13 @@ def make_inputs(cfg, seed: int = 0, attempt: Optional[int] = None, patch=None,
                  k_cache=k_cache, v_cache=v_cache, prefix_lens=_prefix_lens(cfg, seed), acc=acc,
                  plant_rank=_plant_ranks(cfg, seed, acc), zero_init=zero_init)
     if patch is not None:
+        if "plant_rank" in patch:
+            # a patch written for a chosen acceptance pattern names the ranks it planted
+            pr = np.asarray(patch["plant_rank"], dtype=np.int32)
+            if pr.shape != inp.plant_rank.shape:
+                raise ValueError(f"patch plant_rank has shape {pr.shape}, want "
+                                 f"{inp.plant_rank.shape}")
+            inp.plant_rank = pr
         apply_patch(inp, patch)
     return inp
 

@@ -218,13 +218,19 @@ def _fix_heads(ed: _Editor, inp, plan, chain, max_passes: int = 40) -> bool:
     return False
 
 
-def plant(cfg, seed: int, max_attempts: int = 12, verbose: bool = False) -> dict:
-    """Find a patch for (cfg, seed).  Returns the patch dict."""
+def plant(cfg, seed: int, max_attempts: int = 12, verbose: bool = False,
+          ranks=None) -> dict:
+    """Find a patch for (cfg, seed).  Returns the patch dict.
+
+    ``ranks`` ([B, K] ints, -1 = a miss) replaces the ranks drawn from the accuracy
+    table, to reach a chosen accepted length; the patch then records them."""
     if isinstance(cfg, str):
         cfg = get_config(cfg)
     log = print if verbose else (lambda *a, **k: None)
     for attempt in range(max_attempts):
         inp = make_inputs(cfg, seed, attempt=attempt)
+        if ranks is not None:
+            inp.plant_rank = np.asarray(ranks, dtype=np.int32).reshape(cfg.B, cfg.K)
         plan = plan_for(cfg, inp.acc)
         ed = _Editor(inp)
         hf = oracle.as_f64(inp.h, inp.dtype)
@@ -274,6 +280,8 @@ def plant(cfg, seed: int, max_attempts: int = 12, verbose: bool = False) -> dict
             continue
         patch = {"config": cfg.name, "seed": int(seed), "h_attempt": int(attempt), "thr": THR,
                  "ops": ed.ops}
+        if ranks is not None:
+            patch["plant_rank"] = inp.plant_rank.tolist()
         # the patch replayed on a fresh draw must give the same bits
         check = make_inputs(cfg, seed, patch=patch)
         for name, arr in inp.tensors().items():
