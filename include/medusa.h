@@ -200,6 +200,23 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
                                    size_t ws_bytes, void* stream);
 size_t medusa_verify_workspace(const medusa_tree_plan* plan, medusa_dtype dt, int B, int H, int V);
 
+/* medusa_verify_accept without a workspace, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, kernels and results as medusa_verify_accept, minus ws/ws_bytes: the scratch
+ * (per-tile argmax partials; the node argmax when node_argmax is NULL) is a static device
+ * array of MEDUSA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  The call allocates nothing.  Problems whose medusa_verify_workspace()
+ * exceeds that size return MEDUSA_ERR_WORKSPACE before anything is enqueued.  All calls on
+ * one GPU share its array: calls that overlap on one GPU (other streams or threads) race,
+ * so a caller serialises them. */
+#define MEDUSA_NOALLOC_SCRATCH_BYTES 4194304   /* 4 MiB */
+medusa_status medusa_verify_accept_noalloc(const medusa_tree_plan* plan, medusa_dtype dt, int B,
+                                           int H, int V, const void* node_hidden,
+                                           const void* w_lm, const int32_t* node_tokens,
+                                           int32_t* node_argmax, int32_t* accept_len,
+                                           int32_t* accept_nodes, int32_t* accept_tokens,
+                                           float* logits, void* stream);
+
 /* Typical acceptance, for sampling (same section: every candidate whose probability under
  * the base model exceeds a threshold tied to the entropy of that distribution is kept; more
  * tokens pass, exact agreement with the base model's distribution is given up).  The page

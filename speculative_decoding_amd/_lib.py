@@ -48,6 +48,9 @@ _SIGS = {
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_size_t, c_void_p]),
     "medusa_verify_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int, c_int]),
+    "medusa_verify_accept_noalloc": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p,
+                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_void_p]),
     "medusa_verify_accept_typical": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p,
                                              c_void_p, c_void_p, ctypes.c_float, ctypes.c_float,
                                              ctypes.c_float, c_void_p, c_void_p, c_void_p,

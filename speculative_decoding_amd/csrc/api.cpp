@@ -323,6 +323,21 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
                                    int32_t* accept_len, int32_t* accept_nodes,
                                    int32_t* accept_tokens, float* logits, void* ws,
                                    size_t ws_bytes, void* stream) {
+    return medusa::verify_accept_impl(plan, dt, B, H, V, node_hidden, w_lm, node_tokens,
+                                      node_argmax, accept_len, accept_nodes, accept_tokens,
+                                      logits, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// Greedy verification and acceptance on a caller-given scratch area (the workspace, or the
+// library's static scratch in medusa_verify_accept_noalloc).
+medusa_status medusa::verify_accept_impl(const medusa_tree_plan* plan, medusa_dtype dt, int B,
+                                         int H, int V, const void* node_hidden, const void* w_lm,
+                                         const int32_t* node_tokens, int32_t* node_argmax,
+                                         int32_t* accept_len, int32_t* accept_nodes,
+                                         int32_t* accept_tokens, float* logits, void* ws,
+                                         size_t ws_bytes, void* stream) {
     if (!plan || !node_hidden || !w_lm || !node_tokens || !accept_len || !accept_nodes ||
         !accept_tokens)
         return MEDUSA_ERR_NULL;
@@ -367,6 +382,8 @@ medusa_status medusa_verify_accept(const medusa_tree_plan* plan, medusa_dtype dt
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     return MEDUSA_OK;
 }
+
+extern "C" {
 
 size_t medusa_verify_typical_workspace(const medusa_tree_plan* plan, medusa_dtype dt, int B,
                                        int H, int V) {

@@ -175,6 +175,16 @@ hipError_t attention_launch(medusa_dtype dt, const AttnShape& s, const DevicePla
                             const void* k_cache, const void* v_cache, const int32_t* prefix_lens,
                             void* out, void* ws, hipStream_t stream);
 
+// ------------------------------------------------------------------ verify + accept
+// Body of medusa_verify_accept with the scratch area passed in (the caller's workspace, or
+// the static scratch of medusa_verify_accept_noalloc).
+medusa_status verify_accept_impl(const medusa_tree_plan* plan, medusa_dtype dt, int B, int H,
+                                 int V, const void* node_hidden, const void* w_lm,
+                                 const int32_t* node_tokens, int32_t* node_argmax,
+                                 int32_t* accept_len, int32_t* accept_nodes,
+                                 int32_t* accept_tokens, float* logits, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 // ------------------------------------------------------------------ profiling
 void prof_begin(const char* name, hipStream_t stream);
 void prof_end(hipStream_t stream);

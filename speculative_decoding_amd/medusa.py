@@ -15,6 +15,7 @@ from ._lib import lib
 
 MEDUSA_F32, MEDUSA_BF16 = 0, 1
 MEDUSA_MAX_TOPK, MEDUSA_MAX_HEADS, MEDUSA_MAX_NODES = 64, 8, 1024   # limits of include/medusa.h
+MEDUSA_NOALLOC_SCRATCH_BYTES = 4194304   # static scratch of medusa_verify_accept_noalloc
 DTYPES = {"f32": MEDUSA_F32, "bf16": MEDUSA_BF16}
 
 
@@ -262,6 +263,20 @@ def medusa_verify_accept(plan: TreePlan, dt, B, H, V, node_hidden, w_lm, node_to
         _ptr(ws, None, "ws"), ws.numel() * ws.element_size() if ws is not None else 0,
         _stream(stream))
     _check("medusa_verify_accept", st)
+
+
+def medusa_verify_accept_noalloc(plan: TreePlan, dt, B, H, V, node_hidden, w_lm, node_tokens,
+                                 node_argmax, accept_len, accept_nodes, accept_tokens,
+                                 logits=None, stream=None):
+    torch = _torch()
+    st = lib().medusa_verify_accept_noalloc(
+        plan.handle, _dt(dt), B, H, V, _float_ptr(node_hidden, dt, "node_hidden"),
+        _float_ptr(w_lm, dt, "w_lm"), _ptr(node_tokens, torch.int32, "node_tokens"),
+        _ptr(node_argmax, torch.int32, "node_argmax"), _ptr(accept_len, torch.int32, "accept_len"),
+        _ptr(accept_nodes, torch.int32, "accept_nodes"),
+        _ptr(accept_tokens, torch.int32, "accept_tokens"), _ptr(logits, torch.float32, "logits"),
+        _stream(stream))
+    _check("medusa_verify_accept_noalloc", st)
 
 
 def medusa_verify_typical_workspace(plan: TreePlan, dt, B, H, V) -> int:

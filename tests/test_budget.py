@@ -149,6 +149,7 @@ def test_expected_accept_rejects_short_table():
 
 def test_limit_constants_match_header():
     text = open(os.path.join(HERE, "..", "include", "medusa.h")).read()
-    for name in ("MEDUSA_MAX_TOPK", "MEDUSA_MAX_HEADS", "MEDUSA_MAX_NODES"):
+    for name in ("MEDUSA_MAX_TOPK", "MEDUSA_MAX_HEADS", "MEDUSA_MAX_NODES",
+                 "MEDUSA_NOALLOC_SCRATCH_BYTES"):
         v = int(re.search(rf"#define {name} (\d+)", text).group(1))
         assert getattr(M, name) == v, name
