@@ -218,6 +218,22 @@ def rope_rate(torch, M, MedusaStep, Dims, cfg, w, plan, dev, steps: int, warmup:
             "rope_us": 1e3 * ms / n if n else None}
 
 
+def clock_probe(torch, M, reps: int = 3):
+    """Shader clock under MFMA load on every SIMD (medusa_clock_probe): shader-clock ticks
+    over 100 MHz ticks of one workgroup's run; the median of `reps` runs, in MHz."""
+    ticks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    vals = []
+    for _ in range(reps + 1):
+        M.medusa_clock_probe(ticks, sink)
+        torch.cuda.synchronize()
+        t = ticks.cpu().tolist()
+        if t[1] > 0:
+            vals.append(100.0 * t[0] / t[1])
+    vals = vals[1:] or vals
+    return sorted(vals)[len(vals) // 2] if vals else None
+
+
 def hbm_probe(torch, M, buf, reps: int = 10):
     """Read ceiling of this GPU: medusa_hbm_read_probe streaming `buf` (the heads' weights)
     `reps` times, timed with events on the current stream."""
@@ -423,6 +439,7 @@ def main() -> int:
             kernels[name] = {"avg_us": 1e3 * ms / n, "launches": n}
 
     step_us = step_percentiles(torch, step, args.steps)
+    sclk = clock_probe(torch, M)
     probe = hbm_probe(torch, M, w["w2"])
     log(f"[bench] probe {probe['gbps']:.0f} GB/s; step median {step_us['median']:.1f} us")
     res = step.results()
@@ -445,7 +462,8 @@ def main() -> int:
                            args.sweep_steps, max(3, args.sweep_steps // 5))
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "cus": props.multi_processor_count,
-              "arch": getattr(props, "gcnArchName", ""), "hbm_gib": round(props.total_memory / 2**30)}
+              "arch": getattr(props, "gcnArchName", ""), "hbm_gib": round(props.total_memory / 2**30),
+              "sclk_mhz_mfma_load": None if sclk is None else round(sclk, 1)}
     a = [int(x) for x in res["accept_len"]]
     prefix_total = int(np.minimum(inp.prefix_lens, cfg.Lcap).sum())
     ab = algorithmic_bytes(cfg, n_nodes, prefix_total)

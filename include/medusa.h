@@ -277,6 +277,12 @@ medusa_status medusa_advance(const medusa_tree_plan* plan, medusa_dtype dt, int 
  * kernels are compared with.  buf 16-byte aligned and at least 8 KiB. */
 size_t medusa_hbm_probe_bytes(size_t bytes);
 medusa_status medusa_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+/* Clock probe (not part of the method): four workgroups per CU run a chain of bf16 MFMAs
+ * on every SIMD; one wave reads the shader clock counter and the constant 100 MHz counter
+ * before and after its share and writes the two tick counts to ticks[0..1] (device
+ * uint64).  ticks[0] / ticks[1] * 100 MHz is the shader clock under MFMA load.  `sink` (a
+ * device uint32) is written only in an impossible case; it keeps the MFMAs live. */
+medusa_status medusa_clock_probe(uint64_t* ticks, uint32_t* sink, void* stream);
 
 /* ------------------------------------------------------------------ one-layer verifier
  * A stand-in for the frozen base model that scores the tree (not part of the method):

@@ -59,6 +59,7 @@ _SIGS = {
     "medusa_verify_typical_workspace": (c_size_t, [c_void_p, c_int, c_int, c_int, c_int]),
     "medusa_hbm_probe_bytes": (c_size_t, [c_size_t]),
     "medusa_hbm_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "medusa_clock_probe": (c_int, [c_void_p, c_void_p, c_void_p]),
     "medusa_rope": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, ctypes.c_float, c_void_p,
                             c_void_p, c_void_p]),
     "medusa_advance": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,

@@ -279,7 +279,7 @@ size_t medusa_attention_workspace(const medusa_tree_plan* plan, medusa_dtype dt,
     if (!plan || !dtype_ok(dt) || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lcap < 0 ||
         (d != 64 && d != 128))
         return 0;
-    return attn_workspace_bytes(attn_shape(B, plan->n_nodes, Hq, Hkv, d, Lcap));
+    return attn_workspace_bytes(attn_shape(dt, B, plan->n_nodes, Hq, Hkv, d, Lcap));
 }
 
 medusa_status medusa_tree_attention(const medusa_tree_plan* plan, medusa_dtype dt, int B, int Hq,
@@ -297,7 +297,7 @@ medusa_status medusa_tree_attention(const medusa_tree_plan* plan, medusa_dtype d
     if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
         (Lcap > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
         return MEDUSA_ERR_SHAPE;
-    const AttnShape sh = attn_shape(B, plan->n_nodes, Hq, Hkv, d, Lcap);
+    const AttnShape sh = attn_shape(dt, B, plan->n_nodes, Hq, Hkv, d, Lcap);
     if (!ws || ws_bytes < attn_workspace_bytes(sh)) return MEDUSA_ERR_WORKSPACE;
     if (!plan->dev) return MEDUSA_ERR_PLAN_NOT_ON_DEVICE;
     medusa_status st = medusa_internal_device_check();
@@ -509,6 +509,20 @@ medusa_status medusa_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sin
     medusa_status st = medusa_internal_device_check();
     if (st != MEDUSA_OK) return st;
     hipError_t e = hbm_probe_launch(buf, bytes, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return medusa_internal_hip_error(e);
+    return MEDUSA_OK;
+}
+
+medusa_status medusa_clock_probe(uint64_t* ticks, uint32_t* sink, void* stream) {
+    if (!ticks || !sink) return MEDUSA_ERR_NULL;
+    medusa_status st = medusa_internal_device_check();
+    if (st != MEDUSA_OK) return st;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return medusa_internal_hip_error(e);
+    e = clock_probe_launch(reinterpret_cast<unsigned long long*>(ticks), sink, cus > 0 ? cus : 1,
+                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return medusa_internal_hip_error(e);
     return MEDUSA_OK;
 }

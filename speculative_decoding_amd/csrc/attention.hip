@@ -4,17 +4,24 @@
 //
 // Work split.  For one sequence b and one kv head g the query rows are the N*G
 // (node, query head) pairs of that group; they share every key, so they are the M side of
-// two MFMA contractions (scores and the value sum).  A workgroup takes 64 or 128 query rows
-// (16 per wave) and one key range: a chunk of the prefix, or the tree keys.  Each 64-key
-// block is staged in LDS (K row-major, V transposed) and shared by the waves.  Scores
-// are computed transposed, S^T = K Q^T, so each lane owns one query row; its softmax
-// state stays in registers and the value sum O^T = V^T P^T takes P^T straight from the
-// score registers (the two 16-key score tiles give each lane the eight key slots of one
-// 32-deep MFMA step; V^T is read from LDS with the same key order).  For bf16 the
-// probabilities enter that MFMA as a hi + lo pair of bf16 values, so rounding them costs
-// no more than fp32 accumulation would.  Partial (max, sum,
+// two MFMA contractions (scores and the value sum).  A workgroup takes a block of query
+// rows and one key range: a chunk of the prefix, or the tree keys.  Partial (max, sum,
 // unnormalised output) per key range go to the workspace; a second kernel combines them.
 // The ancestor mask is one 64-bit word per (node, 64 keys).
+//
+// bf16 (attn_tile_kernel): 32 x 32 x 16 MFMA tiles, each wave owning 32 or 64 query rows,
+// so every K or V fragment read from LDS feeds one or two MFMAs of 32 x 32 outputs.  Scores
+// are computed transposed, S^T = K Q^T: a lane owns one query column of each 32-row tile
+// (shared with the lane 32 apart) and 16 keys of every 32.  The value sum O^T = V^T P^T
+// takes P^T straight from the score registers as fp16 and V^T from LDS as fp16: bf16 values
+// convert to fp16 exactly from 2^-14 up to 65504, so the probabilities keep 11 significant
+// bits where bf16 keeps 8, in one MFMA instead of a hi + lo pair.  A workgroup whose
+// accumulators come out non-finite (a value beyond fp16's range, or inf/NaN inputs)
+// computes its rows again in fp32 on the vector units.
+// The running maximum is kept lazily: the accumulators are rescaled only when a row's
+// maximum grows by more than 2^8, so probabilities stay below 256 and fp16 holds them.
+//
+// fp32 (attn_partial_kernel): 16 x 16 x 4 fp32 MFMAs, 16 query rows per wave.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -79,31 +86,6 @@ struct AttnArgs {
 };
 
 template <typename T> struct Vt4;
-template <> struct Vt4<bf16_t> {
-    __device__ static __forceinline__ void load2(Frag<bf16_t>& f, const bf16_t* p0, const bf16_t* p1) {
-        const uint2 a = *reinterpret_cast<const uint2*>(p0);
-        const uint2 b = *reinterpret_cast<const uint2*>(p1);
-        f.v = u32x4{a.x, a.y, b.x, b.y};
-    }
-    // p ~= hi + lo with hi = bf16(p) and lo = bf16(p - hi): the value sum runs as two
-    // bf16 MFMAs, so the probabilities keep about 16 significant bits instead of 8.
-    __device__ static __forceinline__ void pack(Frag<bf16_t>& hi, Frag<bf16_t>& lo, const float* p) {
-        uint32_t wh[4], wl[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wh[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
-            wl[i] = pack_bf16x2(p[2 * i] - __uint_as_float(wh[i] << 16),
-                                p[2 * i + 1] - __uint_as_float(wh[i] & 0xFFFF0000u));
-        }
-        hi.v = u32x4{wh[0], wh[1], wh[2], wh[3]};
-        lo.v = u32x4{wl[0], wl[1], wl[2], wl[3]};
-    }
-    static constexpr bool kSplit = true;
-    __device__ static __forceinline__ bf16_t elem(const u32x4& v, int e) {
-        const uint32_t w = v[e >> 1];
-        return (bf16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
-    }
-};
 template <> struct Vt4<float> {
     __device__ static __forceinline__ void load2(Frag<float>& f, const float* p0, const float* p1) {
         f.lo = *reinterpret_cast<const u32x4*>(p0);
@@ -131,7 +113,7 @@ __global__ __launch_bounds__(NWV * 64) void attn_partial_kernel(const AttnArgs a
     __shared__ __align__(16) T Vt[D * VP];
 
     const AttnShape& sh = a.s;
-    const int n_slots = sh.n_splits + 1;
+    const int n_slots = sh.n_slots;
     const int nblocks = sh.B * sh.Hkv * n_slots * sh.n_qblocks;
     int bid = xcd_logical_block(blockIdx.x, nblocks);
     const int qb = bid % sh.n_qblocks;
@@ -338,6 +320,525 @@ __global__ __launch_bounds__(NWV * 64) void attn_partial_kernel(const AttnArgs a
     }
 }
 
+// ------------------------------------------------------------------ bf16: 32 x 32 tiles
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// acc[32x32] += A[32 x 16] * B[16 x 32]: lane l supplies row (l % 32) of A and column
+// (l % 32) of B at contraction slots 8*(l/32) .. 8*(l/32)+7 (any slot -> index map shared by
+// A and B is allowed).  Lane l holds acc[8*(v/4) + 4*(l/32) + v%4][l % 32] in register v.
+__device__ __forceinline__ void mma32_bf16(floatx16& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32_f16(floatx16& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+// Two fp32 values as one word of fp16 (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    const f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+// Element e (0..7) of eight bf16 values held as four words, as fp32 (exact).
+__device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
+    const uint32_t w = v[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+// The rows [row0, row0 + nrows) of one (sequence, kv head) over one key range, in fp32 on
+// the vector units straight from global memory, one row per thread: scores, their maximum
+// and sum, then the unnormalised output 32 head-dim elements at a time.  Written for
+// correctness only: it serves the rare key range whose fp16 value path overflowed.  Kept
+// out of line so that it adds no registers to the tiled kernel.
+template <int D>
+__device__ __noinline__ void attn_rows_fp32(const bf16_t* q, const bf16_t* kpre, const bf16_t* vpre,
+                                            const bf16_t* ktr, const bf16_t* vtr,
+                                            const uint64_t* mask, int mask_words, float* wo_base,
+                                            float* ml_base, int rows, int N, int G, int Hq,
+                                            int g, long long kstride, float scale_log2, int row0,
+                                            int nrows, int p_begin, int p_end, bool with_tree) {
+    const int r = row0 + (int)threadIdx.x;
+    if ((int)threadIdx.x >= nrows || r >= rows) return;
+    const int node = r / G;
+    const int head = g * G + r % G;
+    const bf16_t* qr = q + ((long long)node * Hq + head) * D;
+    // keys j < n_pre are prefix rows p_begin + j; the next N (with_tree) are tree rows
+    const int n_pre = p_end - p_begin;
+    const int n_all = n_pre + (with_tree ? N : 0);
+    auto row_k = [&](int j) { return j < n_pre ? kpre + (p_begin + j) * kstride : ktr + (j - n_pre) * kstride; };
+    auto row_v = [&](int j) { return j < n_pre ? vpre + (p_begin + j) * kstride : vtr + (j - n_pre) * kstride; };
+    auto visible = [&](int j) {
+        if (j < n_pre) return true;
+        const int m = j - n_pre;
+        return ((mask[(long long)node * mask_words + (m >> 6)] >> (m & 63)) & 1ull) != 0;
+    };
+    auto score = [&](int j) {
+        const bf16_t* kr = row_k(j);
+        float s = 0.f;
+        for (int e = 0; e < D; ++e) s += bf16_to_f32(qr[e]) * bf16_to_f32(kr[e]);
+        return s * scale_log2;
+    };
+    float m = -INFINITY;
+    for (int j = 0; j < n_all; ++j)
+        if (visible(j)) m = fmaxf(m, score(j));
+    const float mb = m == -INFINITY ? 0.f : m;
+    float l = 0.f;
+    for (int j = 0; j < n_all; ++j)
+        if (visible(j)) l += exp2f(score(j) - mb);
+    float* wo = wo_base + (long long)r * D;
+    for (int c = 0; c < D; c += 32) {
+        float acc[32];
+        for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+        for (int j = 0; j < n_all; ++j) {
+            if (!visible(j)) continue;
+            const float p = exp2f(score(j) - mb);
+            const bf16_t* vr = row_v(j) + c;
+            for (int e = 0; e < 32; ++e) acc[e] += p * bf16_to_f32(vr[e]);
+        }
+        for (int e = 0; e < 32; ++e) wo[c + e] = acc[e];
+    }
+    ml_base[2 * r + 0] = m;
+    ml_base[2 * r + 1] = l;
+}
+
+// Compile-time tuning overrides (0: chosen from the shape).
+#ifndef MEDUSA_ATTN_R
+#define MEDUSA_ATTN_R 0
+#endif
+#ifndef MEDUSA_ATTN_SPLITS
+#define MEDUSA_ATTN_SPLITS 0
+#endif
+#ifndef MEDUSA_ATTN_PRIO
+#define MEDUSA_ATTN_PRIO 0    // raise the wave priority around its MFMA runs
+#endif
+
+constexpr int kTileWaves = 4;
+constexpr int kTileThreads = kTileWaves * 64;
+constexpr int kTileKeys = 64;       // keys per LDS block
+constexpr float kLazyMax = 8.f;     // rescale once a row maximum grows by more than 2^8
+
+// R: 32-row query tiles per wave (1 or 2); D: head dim (64 or 128).
+template <int D, int R>
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(R == 1 ? 2 : 1)))
+void attn_tile_kernel(const AttnArgs a) {
+    constexpr int KB = kTileKeys;
+    constexpr int KP = D + 8;            // K row pitch: rows 4 banks apart, 8 rows cover 32
+    constexpr int VP = KB + 8;           // V^T row pitch: rows 4 banks apart, 8 rows cover 32
+    constexpr int KS = D / 16;           // 16-deep steps over the head dim
+    constexpr int DT = D / 32;           // 32-row tiles of O^T over the head dim
+    constexpr int ROWS = 32 * R * kTileWaves;
+    constexpr int KVEC = KB * D / 8;                 // 16-byte K pieces per block
+    constexpr int KPT = KVEC / kTileThreads;         // ... per thread
+    constexpr int VUNITS = (KB / 4) * (D / 8);       // V units: 4 keys x 8 head-dim elements
+    static_assert(KPT * kTileThreads == KVEC, "K block split over the threads");
+    static_assert(VUNITS <= kTileThreads, "one V unit per thread at most");
+    __shared__ __align__(16) bf16_t Ks[2][KB * KP];
+    __shared__ __align__(16) uint16_t Vt[2][D * VP];
+
+    const AttnShape& sh = a.s;
+    const int n_slots = sh.n_slots;
+    const int nblocks = sh.B * sh.Hkv * n_slots * sh.n_qblocks;
+    int bid = xcd_logical_block(blockIdx.x, nblocks);
+    const int qb = bid % sh.n_qblocks;
+    bid /= sh.n_qblocks;
+    const int slot = bid % n_slots;
+    bid /= n_slots;
+    const int g = bid % sh.Hkv;
+    const int b = bid / sh.Hkv;
+
+    // the prefix length is uniform: keep it (and every loop bound) in scalar registers.
+    // Slot s takes prefix keys [s chunk, (s+1) chunk) up to L; the last live slot (slot 0
+    // for an empty prefix) also takes the tree keys.
+    const int L = min(max(__builtin_amdgcn_readfirstlane(a.prefix_lens[b]), 0), sh.Lcap);
+    const int last = L > 0 ? (L - 1) / sh.chunk : 0;
+    if (slot > last) return;           // empty prefix chunk: the combine skips this slot
+    const int p_begin = slot * sh.chunk;
+    const int p_end = min(L, p_begin + sh.chunk);
+    const bool with_tree = slot == last;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    // Q^T operands: lane l holds query row (tile base + l % 32) at head-dim slots
+    // 16 ks + 8 (l / 32) .. + 7 of every 16-deep step.
+    u32x4 qf[R][KS];
+    int node[R];
+    bool row_ok[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int r = qb * ROWS + (wave * R + t) * 32 + l32;
+        row_ok[t] = r < sh.rows;
+        node[t] = row_ok[t] ? r / sh.G : 0;
+        const int head = g * sh.G + (row_ok[t] ? r % sh.G : 0);
+        const bf16_t* q = static_cast<const bf16_t*>(a.q) +
+                          (((long long)b * sh.N + node[t]) * sh.Hq + head) * D + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[t][ks] = row_ok[t] ? *reinterpret_cast<const u32x4*>(q + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    const bf16_t* const kpre = static_cast<const bf16_t*>(a.k_cache) + ((long long)b * sh.Lcap * sh.Hkv + g) * D;
+    const bf16_t* const vpre = static_cast<const bf16_t*>(a.v_cache) + ((long long)b * sh.Lcap * sh.Hkv + g) * D;
+    const bf16_t* const ktr = static_cast<const bf16_t*>(a.k_tree) + ((long long)b * sh.N * sh.Hkv + g) * D;
+    const bf16_t* const vtr = static_cast<const bf16_t*>(a.v_tree) + ((long long)b * sh.N * sh.Hkv + g) * D;
+    const long long kstride = (long long)sh.Hkv * D;   // elements between consecutive keys
+    // the key range the loop below walks: the prefix chunk, then the tree keys
+    const bf16_t* ksrc = kpre;
+    const bf16_t* vsrc = vpre;
+    int k_begin = p_begin, k_end = p_end;
+
+    // Staging.  K: consecutive threads take consecutive 16-byte pieces of a key row.  V: a
+    // thread takes one unit of 4 consecutive keys x 8 head-dim elements (four 16-byte
+    // loads) and writes each element's 4 keys as one 8-byte word of V^T; the 16 lanes that
+    // share an element write 128 consecutive bytes.
+    // Per-lane offsets (elements) within a block; the block's base pointer is uniform.
+    int kkey[KPT], koff[KPT], kls[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int idx = tid + j * kTileThreads;
+        kkey[j] = idx / (D / 8);
+        koff[j] = kkey[j] * (int)kstride + (idx % (D / 8)) * 8;
+        kls[j] = kkey[j] * KP + (idx % (D / 8)) * 8;
+    }
+    constexpr bool kAllV = VUNITS == kTileThreads;
+    const bool vact = kAllV || tid < VUNITS;
+    const int vq = tid % (KB / 4);      // key quad
+    const int vp = tid / (KB / 4);      // head-dim piece of 8
+    const int voff = 4 * vq * (int)kstride + vp * 8;
+    // V^T keeps each 16-key group permuted (key 8a + 4b + c at 8b + 4a + c), so the eight
+    // keys one lane feeds to a value MFMA are eight consecutive elements: one 16-byte read
+    const int vls = (8 * vp) * VP + 4 * ((vq & ~3) | ((vq & 1) << 1) | ((vq >> 1) & 1));
+    u32x4 kr[KPT], vr[4];
+    auto fetch = [&](int kb0) {
+        const bf16_t* kb = ksrc + (long long)kb0 * kstride;
+        const bf16_t* vb = vsrc + (long long)kb0 * kstride;
+        if (kb0 + KB <= k_end) {          // a whole block: no per-key tests
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) kr[j] = *reinterpret_cast<const u32x4*>(kb + koff[j]);
+            if (vact) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vr[i] = *reinterpret_cast<const u32x4*>(vb + voff + i * (int)kstride);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                kr[j] = u32x4{0u, 0u, 0u, 0u};
+                if (kb0 + kkey[j] < k_end) kr[j] = *reinterpret_cast<const u32x4*>(kb + koff[j]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vr[i] = u32x4{0u, 0u, 0u, 0u};
+                if (vact && kb0 + 4 * vq + i < k_end)
+                    vr[i] = *reinterpret_cast<const u32x4*>(vb + voff + i * (int)kstride);
+            }
+        }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) *reinterpret_cast<u32x4*>(&Ks[buf][kls[j]]) = kr[j];
+        if (vact) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {      // fp16: exact in fp16's normal range
+                uint2 w;
+                w.x = pack_f16x2(bf16_elem(vr[0], e), bf16_elem(vr[1], e));
+                w.y = pack_f16x2(bf16_elem(vr[2], e), bf16_elem(vr[3], e));
+                *reinterpret_cast<uint2*>(&Vt[buf][vls + e * VP]) = w;
+            }
+        }
+    };
+
+    floatx16 o[R][DT];
+    float m_used[R], l_sum[R];
+
+    // One 64-key block out of LDS buffer `buf`, as two 32-key halves: scores, lazily
+    // rescaled softmax, value sum.  Register v of score tile sc[t] is key
+    // kb0 + 32 h + 8 (v/4) + 4 hi + v%4.  MASK: 0 a whole prefix block, 1 the prefix's last
+    // block (keys past the end), 2 tree keys (the ancestor mask; it has no bit past the
+    // last node, whose K/V rows stage as zeros).
+    const float c2 = a.scale_log2;
+    auto block = [&](int buf, int kb0, auto mask_tag) {
+        constexpr int MASK = decltype(mask_tag)::value;
+        uint64_t mw[R];
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+            mw[t] = (MASK == 2 && row_ok[t]) ? a.plan.mask[(long long)node[t] * a.plan.mask_words + (kb0 >> 6)] : 0ull;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (MASK != 0 && kb0 + 32 * h >= k_end) break;
+            floatx16 sc[R];
+#pragma unroll
+            for (int t = 0; t < R; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sc[t][v] = 0.f;
+            if (MEDUSA_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(&Ks[buf][(32 * h + l32) * KP + 16 * ks + 8 * hi]);
+#pragma unroll
+                for (int t = 0; t < R; ++t) mma32_bf16(sc[t], kf, qf[t][ks]);
+            }
+            if (MEDUSA_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
+            // row maxima of the raw scores (the scale is positive), masked keys at -inf
+            float mx[R];
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                if (MASK == 2) {
+                    const uint32_t bits = (uint32_t)(mw[t] >> (32 * h + 4 * hi));
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (!((bits >> (8 * (v >> 2) + (v & 3))) & 1u)) sc[t][v] = -INFINITY;
+                } else if (MASK == 1) {
+                    const int left = k_end - (kb0 + 32 * h + 4 * hi);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (8 * (v >> 2) + (v & 3) >= left) sc[t][v] = -INFINITY;
+                }
+                float m = sc[t][0];
+#pragma unroll
+                for (int v = 1; v < 16; ++v) m = fmaxf(m, sc[t][v]);
+                mx[t] = max_xor32(m) * c2;
+            }
+            bool grow = false;
+#pragma unroll
+            for (int t = 0; t < R; ++t) grow |= mx[t] > m_used[t] + kLazyMax;
+            if (__any(grow)) {
+#pragma unroll
+                for (int t = 0; t < R; ++t) {
+                    const float m_new = fmaxf(m_used[t], mx[t]);
+                    const float alpha = m_used[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used[t] - m_new);
+                    l_sum[t] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+                    m_used[t] = m_new;
+                }
+            }
+            // probabilities p = 2^(s c - m) as the P^T operands: pf[t][kk] holds registers
+            // 8 kk .. 8 kk + 7
+            u32x4 pf[R][2];
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                const float mb = m_used[t] == -INFINITY ? 0.f : m_used[t];
+                float ls = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * kk + 2 * w], c2, -mb));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * kk + 2 * w + 1], c2, -mb));
+                        pf[t][kk][w] = pack_f16x2(p0, p1);
+                        ls += p0 + p1;
+                    }
+                l_sum[t] += ls;
+            }
+            // value sum: V^T rows 32 dt + l % 32, the eight keys of this lane's P^T slots
+            if (MEDUSA_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const u32x4 vf = *reinterpret_cast<const u32x4*>(
+                        &Vt[buf][(32 * dt + l32) * VP + 32 * h + 16 * kk + 8 * hi]);
+#pragma unroll
+                    for (int t = 0; t < R; ++t) mma32_f16(o[t][dt], vf, pf[t][kk]);
+                }
+            if (MEDUSA_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
+        }
+    };
+    using NoMask = std::integral_constant<int, 0>;
+    using BoundMask = std::integral_constant<int, 1>;
+    using TreeMask = std::integral_constant<int, 2>;
+
+    // The whole key range, double-buffered: block j+1 is written into the other LDS buffer
+    // while block j is used, and the loads of block j+2 are issued right after; one barrier
+    // per block.  Every block but the last is whole; the last, which may end inside the
+    // block, runs after the loop.  The tree keys and a prefix chunk run separate copies of
+    // the loop (with and without the ancestor mask).
+    auto run = [&](auto tree_tag) {
+        constexpr bool TREE = decltype(tree_tag)::value;
+        fetch(k_begin);
+        stage(0);
+        if (k_begin + KB < k_end) fetch(k_begin + KB);
+        __syncthreads();
+        int buf = 0;
+        int kb0 = k_begin;
+        for (; kb0 + KB < k_end; kb0 += KB) {
+            if (TREE) block(buf, kb0, TreeMask{});
+            else block(buf, kb0, NoMask{});
+            stage(buf ^ 1);
+            if (kb0 + 2 * KB < k_end) fetch(kb0 + 2 * KB);
+            __syncthreads();
+            buf ^= 1;
+        }
+        if (TREE) block(buf, kb0, TreeMask{});
+        else if (kb0 + KB == k_end) block(buf, kb0, NoMask{});
+        else block(buf, kb0, BoundMask{});
+        __syncthreads();       // the LDS buffers are free again
+    };
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        m_used[t] = -INFINITY;
+        l_sum[t] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[t][dt][v] = 0.f;
+    }
+    if (p_begin < p_end) run(std::false_type{});
+    if (with_tree) {
+        ksrc = ktr;
+        vsrc = vtr;
+        k_begin = 0;
+        k_end = sh.N;
+        run(std::true_type{});
+    }
+
+    // A value beyond fp16's range (or an inf/NaN input) leaves a non-finite accumulator:
+    // the workgroup's rows are then computed again in fp32 on the vector units.
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) bad |= !__builtin_isfinite(o[t][dt][v]);
+    const long long slot_base = (((long long)b * sh.Hkv + g) * n_slots + slot) * sh.rows;
+    bf16_t* const out = static_cast<bf16_t*>(a.out);
+    const bool fallback = __syncthreads_or(bad);
+    if (fallback)
+        attn_rows_fp32<D>(static_cast<const bf16_t*>(a.q) + (long long)b * sh.N * sh.Hq * D, kpre,
+                          vpre, ktr, vtr, a.plan.mask, a.plan.mask_words, a.ws_o + slot_base * D,
+                          a.ws_ml + slot_base * 2, sh.rows, sh.N, sh.G, sh.Hq, g, kstride,
+                          a.scale_log2, qb * ROWS, ROWS, p_begin, p_end, with_tree);
+
+    // The only live slot of its row block writes the attention output straight from its
+    // registers.
+    if (last == 0 && !fallback) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            const float inv = 1.f / sum_xor32(l_sum[t]);
+            if (!row_ok[t]) continue;
+            const int r = qb * ROWS + (wave * R + t) * 32 + l32;
+            bf16_t* orow = out + (((long long)b * sh.N + r / sh.G) * sh.Hq + g * sh.G + r % sh.G) * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * j + 4 * hi) =
+                        uint2{pack_bf16x2(o[t][dt][4 * j] * inv, o[t][dt][4 * j + 1] * inv),
+                              pack_bf16x2(o[t][dt][4 * j + 2] * inv, o[t][dt][4 * j + 3] * inv)};
+        }
+        return;
+    }
+
+    // After the fp32 recomputation, the only live slot normalises the partial it wrote.
+    if (last == 0) {
+        __syncthreads();
+        for (int i = tid; i < ROWS * (D / 8); i += kTileThreads) {
+            const int r = qb * ROWS + i / (D / 8);
+            if (r >= sh.rows) continue;
+            const int part = i % (D / 8);
+            const long long bs = slot_base + r;
+            const float inv = 1.f / a.ws_ml[bs * 2 + 1];
+            const floatx4* src = reinterpret_cast<const floatx4*>(a.ws_o + bs * D + part * 8);
+            const floatx4 v0 = src[0], v1 = src[1];
+            bf16_t* orow = out + (((long long)b * sh.N + r / sh.G) * sh.Hq + g * sh.G + r % sh.G) * D + part * 8;
+            *reinterpret_cast<u32x4*>(orow) =
+                u32x4{pack_bf16x2(v0[0] * inv, v0[1] * inv), pack_bf16x2(v0[2] * inv, v0[3] * inv),
+                      pack_bf16x2(v1[0] * inv, v1[1] * inv), pack_bf16x2(v1[2] * inv, v1[3] * inv)};
+        }
+        return;
+    }
+
+    // Otherwise the partial (unnormalised output, running maximum, sum) goes to the
+    // workspace for attn_merge_kernel.
+    if (!fallback) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            const float l_row = sum_xor32(l_sum[t]);
+            if (!row_ok[t]) continue;
+            const int r = qb * ROWS + (wave * R + t) * 32 + l32;
+            const long long base = slot_base + r;
+            float* wo = a.ws_o + base * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<floatx4*>(wo + 32 * dt + 8 * j + 4 * hi) =
+                        floatx4{o[t][dt][4 * j], o[t][dt][4 * j + 1], o[t][dt][4 * j + 2], o[t][dt][4 * j + 3]};
+            if (hi == 0) {
+                a.ws_ml[base * 2 + 0] = m_used[t];
+                a.ws_ml[base * 2 + 1] = l_row;
+            }
+        }
+    }
+}
+
+// bf16: merge the partials of the row blocks that have more than one live slot (a row
+// block whose only live slot wrote its output directly is skipped).  Sixteen threads per
+// query row, eight head-dim elements each; every slot's loads are issued before they are
+// used.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
+    constexpr int TPR = D / 8;                       // threads per row
+    const AttnShape& sh = a.s;
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)sh.B * sh.Hkv * sh.rows * TPR;
+    if (gid >= total) return;
+    const int part = (int)(gid % TPR);
+    const long long row_id = gid / TPR;              // (b, g, r)
+    const int r = (int)(row_id % sh.rows);
+    const int bg = (int)(row_id / sh.rows);
+    const int b = bg / sh.Hkv;
+    const int g = bg % sh.Hkv;
+    const int L = min(max(a.prefix_lens[b], 0), sh.Lcap);
+    const int last = L > 0 ? (L - 1) / sh.chunk : 0;
+    if (last == 0) return;
+    const long long base0 = (long long)bg * sh.n_slots * sh.rows + r;
+    // one pass with a running maximum, four slots' loads in flight at a time
+    float mx = -INFINITY, den = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 <= last; s0 += 4) {
+        float ms[4], ls[4];
+        floatx4 v0[4], v1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int sl = min(s0 + u, last);
+            const long long bs = base0 + (long long)sl * sh.rows;
+            ms[u] = a.ws_ml[bs * 2];
+            ls[u] = a.ws_ml[bs * 2 + 1];
+            const floatx4* src = reinterpret_cast<const floatx4*>(a.ws_o + bs * D + part * 8);
+            v0[u] = src[0];
+            v1[u] = src[1];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (s0 + u > last || ms[u] == -INFINITY) continue;
+            const float m_new = fmaxf(mx, ms[u]);
+            const float alpha = mx == -INFINITY ? 0.f : exp2f(mx - m_new);
+            const float w = exp2f(ms[u] - m_new);
+            den = den * alpha + w * ls[u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] = acc[e] * alpha + w * v0[u][e];
+                acc[4 + e] = acc[4 + e] * alpha + w * v1[u][e];
+            }
+            mx = m_new;
+        }
+    }
+    const float inv = 1.f / den;
+    bf16_t* orow = static_cast<bf16_t*>(a.out) +
+                   (((long long)b * sh.N + r / sh.G) * sh.Hq + g * sh.G + r % sh.G) * D + part * 8;
+    *reinterpret_cast<u32x4*>(orow) =
+        u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+              pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+}
+
 // One wave per (sequence, node, query head): combine the key ranges.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnArgs a) {
@@ -352,8 +853,16 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnArgs a
     const int b = row_id / (sh.Hq * sh.N);
     const int g = j / sh.G;
     const int r = i * sh.G + (j - g * sh.G);
-    const int n_slots = sh.n_splits + 1;
+    const int n_slots = sh.n_slots;
     const int L = min(max(a.prefix_lens[b], 0), sh.Lcap);
+    // live slots: prefix chunks that hold keys, and the tree keys (their own slot, or the
+    // last live chunk's)
+    const int last = L > 0 ? (L - 1) / sh.chunk : 0;
+    auto is_live = [&](int s) {
+        if (s >= n_slots) return false;
+        if (sh.tree_merged) return s <= last;
+        return s == sh.n_splits || s * sh.chunk < L;
+    };
 
     // every lane fetches one slot's (max, sum) so the slots are read in parallel
     const long long base0 = (((long long)b * sh.Hkv + g) * n_slots) * sh.rows + r;
@@ -364,7 +873,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnArgs a
     float mx = -INFINITY;
     for (int s0 = 0; s0 < n_slots; s0 += kWave) {
         const int s = s0 + lane;
-        const bool live = s < n_slots && (s == sh.n_splits || s * sh.chunk < L);
+        const bool live = is_live(s);
         const float ms = live ? a.ws_ml[(base0 + (long long)s * sh.rows) * 2] : -INFINITY;
         float m = ms;
 #pragma unroll
@@ -373,7 +882,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnArgs a
     }
     for (int s0 = 0; s0 < n_slots; s0 += kWave) {
         const int s = s0 + lane;
-        const bool live = s < n_slots && (s == sh.n_splits || s * sh.chunk < L);
+        const bool live = is_live(s);
         const long long bs = base0 + (long long)s * sh.rows;
         const float w = live ? exp2f(a.ws_ml[bs * 2] - mx) : 0.f;
         float part = live ? w * a.ws_ml[bs * 2 + 1] : 0.f;
@@ -408,55 +917,101 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnArgs a
 template <typename T, int D>
 hipError_t launch_td(const AttnArgs& a, hipStream_t stream) {
     const AttnShape& s = a.s;
-    const int nblocks = s.B * s.Hkv * (s.n_splits + 1) * s.n_qblocks;
-    prof_begin("attn_partial", stream);
-    if (s.waves == kAttnWavesLarge)
-        hipLaunchKernelGGL((attn_partial_kernel<T, D, kAttnWavesLarge>), dim3(nblocks),
-                           dim3(kAttnWavesLarge * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL((attn_partial_kernel<T, D, kAttnWavesSmall>), dim3(nblocks),
-                           dim3(kAttnWavesSmall * 64), 0, stream, a);
-    prof_end(stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int rows = s.B * s.N * s.Hq;
-    prof_begin("attn_combine", stream);
-    hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((rows + 3) / 4), dim3(kThreads), 0, stream, a);
-    prof_end(stream);
-    return hipGetLastError();
+    const int nblocks = s.B * s.Hkv * s.n_slots * s.n_qblocks;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        prof_begin("attn_partial", stream);
+        if (s.tile_r == 2)
+            hipLaunchKernelGGL((attn_tile_kernel<D, 2>), dim3(nblocks), dim3(kTileThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((attn_tile_kernel<D, 1>), dim3(nblocks), dim3(kTileThreads), 0, stream, a);
+        prof_end(stream);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const long long threads = (long long)s.B * s.Hkv * s.rows * (D / 8);
+        prof_begin("attn_combine", stream);
+        hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                           stream, a);
+        prof_end(stream);
+        return hipGetLastError();
+    } else {
+        prof_begin("attn_partial", stream);
+        if (s.waves == kAttnWavesLarge)
+            hipLaunchKernelGGL((attn_partial_kernel<T, D, kAttnWavesLarge>), dim3(nblocks),
+                               dim3(kAttnWavesLarge * 64), 0, stream, a);
+        else
+            hipLaunchKernelGGL((attn_partial_kernel<T, D, kAttnWavesSmall>), dim3(nblocks),
+                               dim3(kAttnWavesSmall * 64), 0, stream, a);
+        prof_end(stream);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int rows = s.B * s.N * s.Hq;
+        prof_begin("attn_combine", stream);
+        hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((rows + 3) / 4), dim3(kThreads), 0, stream, a);
+        prof_end(stream);
+        return hipGetLastError();
+    }
 }
 
 }  // namespace
 
-AttnShape attn_shape(int B, int N, int Hq, int Hkv, int d, int Lcap) {
+AttnShape attn_shape(medusa_dtype dt, int B, int N, int Hq, int Hkv, int d, int Lcap) {
     AttnShape s{};
     s.B = B; s.N = N; s.Hq = Hq; s.Hkv = Hkv; s.d = d; s.Lcap = Lcap;
     s.G = Hq / Hkv;
     s.rows = N * s.G;
-    s.waves = s.rows >= kAttnLargeRows ? kAttnWavesLarge : kAttnWavesSmall;
-    s.n_qblocks = (s.rows + 16 * s.waves - 1) / (16 * s.waves);
-    // Split the prefix so that (a) the partial outputs (rows * d fp32 per split) stay
-    // below about half the K/V bytes they summarise and (b) the grid still covers the
-    // chip when there are few (sequence, kv head, query block) triples.
     const int max_splits = Lcap > 0 ? (Lcap + kKeys - 1) / kKeys : 1;
-    int splits = Lcap / (2 * s.rows);
-    const int base = B * Hkv * s.n_qblocks;
-    // about 1024 waves in flight: with 2048 (twice the splits) the 8B tree took 22.6 + 8.9
-    // us, against 22.2 + 7.8 here (7B shape 15.7 + 8.9 against 13.2 + 8.1)
-    const int fill_blocks = 1024 / s.waves;
-    const int fill = (fill_blocks + base - 1) / base;
-    if (splits < fill) splits = fill;
+    int splits;
+    if (dt == MEDUSA_BF16) {
+        // 32 x 32 tiles: two per wave once a kv head has 256 query rows (each K/V fragment
+        // then feeds two MFMAs), one below.  Prefix splits give about `target` workgroups.
+        s.tile_r = 1;
+#if MEDUSA_ATTN_R
+        s.tile_r = MEDUSA_ATTN_R;
+#endif
+        s.waves = kTileWaves;
+        const int per = 32 * s.tile_r * kTileWaves;
+        s.n_qblocks = (s.rows + per - 1) / per;
+        // prefix chunks: about 256 workgroups over the (sequence, kv head, row block)
+        // units, 4 to 12 chunks each, at least 256 keys per chunk.  Measured (us, tile +
+        // merge; best in brackets): 8B shape 16 units -> 12 chunks 22.4 + 10.7 [33.1; 4:
+        // 42, 8: 34.7]; 7B shape 32 -> 4 chunks 16.6 + 7.1 [6: 22.5]; dense tree 64 -> 4
+        // 70.0 + 8.1 [6: 75.7]; batched 70B 256 -> 4 147.9 + 10.4 [best]
+        const int base = B * Hkv * s.n_qblocks;
+        splits = (256 + base / 2) / base;
+        if (splits < 4) splits = 4;
+        if (splits > 12) splits = 12;
+        const int by_len = Lcap / 256;
+        if (splits > by_len) splits = by_len;
+#if MEDUSA_ATTN_SPLITS
+        splits = MEDUSA_ATTN_SPLITS;
+#endif
+    } else {
+        s.tile_r = 0;
+        s.waves = s.rows >= kAttnLargeRows ? kAttnWavesLarge : kAttnWavesSmall;
+        s.n_qblocks = (s.rows + 16 * s.waves - 1) / (16 * s.waves);
+        // Split the prefix so that (a) the partial outputs (rows * d fp32 per split) stay
+        // below about half the K/V bytes they summarise and (b) the grid still covers the
+        // chip when there are few (sequence, kv head, query block) triples: about 1024
+        // waves in flight.
+        splits = Lcap / (2 * s.rows);
+        const int base = B * Hkv * s.n_qblocks;
+        const int fill_blocks = 1024 / s.waves;
+        const int fill = (fill_blocks + base - 1) / base;
+        if (splits < fill) splits = fill;
+    }
     if (splits < 1) splits = 1;
     if (splits > max_splits) splits = max_splits;
     int chunk = Lcap > 0 ? (Lcap + splits - 1) / splits : kKeys;
     chunk = (chunk + kKeys - 1) / kKeys * kKeys;
     s.chunk = chunk;
     s.n_splits = Lcap > 0 ? (Lcap + chunk - 1) / chunk : 0;
+    s.tree_merged = dt == MEDUSA_BF16 ? 1 : 0;
+    s.n_slots = s.tree_merged ? (s.n_splits > 0 ? s.n_splits : 1) : s.n_splits + 1;
     return s;
 }
 
 size_t attn_workspace_bytes(const AttnShape& s) {
-    const size_t slots = (size_t)s.n_splits + 1;
+    const size_t slots = (size_t)s.n_slots;
     const size_t rows = (size_t)s.B * s.Hkv * slots * s.rows;
     return rows * (size_t)s.d * sizeof(float) + rows * 2 * sizeof(float) + 256;
 }
@@ -472,7 +1027,7 @@ hipError_t attention_launch(medusa_dtype dt, const AttnShape& s, const DevicePla
     a.q = q; a.k_tree = k_tree; a.v_tree = v_tree; a.k_cache = k_cache; a.v_cache = v_cache;
     a.prefix_lens = prefix_lens;
     a.out = out;
-    const size_t slots = (size_t)s.n_splits + 1;
+    const size_t slots = (size_t)s.n_slots;
     const size_t rows = (size_t)s.B * s.Hkv * slots * s.rows;
     a.ws_o = static_cast<float*>(ws);
     a.ws_ml = a.ws_o + rows * s.d;

@@ -163,12 +163,15 @@ struct AttnShape {
     int B, N, Hq, Hkv, d, Lcap;
     int G;          // Hq / Hkv
     int rows;       // N * G query rows per (sequence, kv head)
-    int waves;      // waves (16 query rows each) per workgroup
-    int n_qblocks;  // ceil(rows / (16 * waves))
+    int waves;      // waves per workgroup
+    int tile_r;     // bf16: 32-row query tiles per wave (1 or 2); fp32: 0 (16 rows per wave)
+    int n_qblocks;  // query-row blocks per (sequence, kv head)
     int chunk;      // prefix keys per split (multiple of 64)
-    int n_splits;   // prefix splits; one more slot holds the tree keys
+    int n_splits;   // prefix splits
+    int tree_merged;  // 1: the tree keys join the last live prefix chunk; 0: a slot of their own
+    int n_slots;    // partial results per (sequence, kv head, query row)
 };
-AttnShape attn_shape(int B, int N, int Hq, int Hkv, int d, int Lcap);
+AttnShape attn_shape(medusa_dtype dt, int B, int N, int Hq, int Hkv, int d, int Lcap);
 size_t attn_workspace_bytes(const AttnShape& s);
 hipError_t attention_launch(medusa_dtype dt, const AttnShape& s, const DevicePlan& plan, float scale,
                             const void* q, const void* k_tree, const void* v_tree,

@@ -1,4 +1,5 @@
-// HBM read-bandwidth probe: the ceiling the streaming kernels are measured against.
+// HBM read-bandwidth probe: the ceiling the streaming kernels are measured against; and a
+// clock probe (the shader clock under MFMA load).
 //
 // Every wave streams whole 8 KiB blocks of the buffer with the access pattern of the GEMV
 // kernel (64 lanes x 16 contiguous bytes per instruction, non-temporal), four blocks in
@@ -41,7 +42,46 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_probe_kernel(const u32x4* _
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Clock probe: every workgroup runs a long chain of bf16 MFMAs on every SIMD (the load of
+// the MFMA-bound kernels); the first wave of workgroup 0 reads the shader clock counter
+// (s_memtime) and the constant 100 MHz counter (s_memrealtime) before and after its share,
+// so their ratio is the shader clock under that load.
+constexpr int kClockIters = 4096;
+
+__global__ __launch_bounds__(256) void clock_probe_kernel(unsigned long long* out, uint32_t* sink) {
+    const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
+    unsigned long long t0 = 0, r0 = 0;
+    if (timer) {
+        t0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    const u32x4 a = {threadIdx.x, 1u, 2u, 3u};
+    const u32x4 b = {3u, 2u, 1u, threadIdx.x};
+    floatx16 acc0 = {}, acc1 = {};
+    for (int i = 0; i < kClockIters; ++i) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
+                                                       __builtin_bit_cast(bf16x8, a), acc1, 0, 0, 0);
+    }
+    if (timer) {
+        const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+        const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+        out[0] = t1 - t0;
+        out[1] = r1 - r0;
+    }
+    float s = 0.f;
+    for (int v = 0; v < 16; ++v) s += acc0[v] + acc1[v];
+    if (s == 1234.5f) sink[0] = 1u;     // keeps the MFMAs live
+}
+
 }  // namespace
+
+hipError_t clock_probe_launch(unsigned long long* out, uint32_t* sink, int cus, hipStream_t stream) {
+    // four workgroups of four waves per CU: every SIMD runs four waves of MFMAs
+    hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)(4 * cus)), dim3(256), 0, stream, out, sink);
+    return hipGetLastError();
+}
 
 long long hbm_probe_bytes(size_t bytes) {
     return (long long)(bytes / kProbeBlockBytes) * kProbeBlockBytes;

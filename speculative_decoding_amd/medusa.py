@@ -320,6 +320,14 @@ def medusa_hbm_read_probe(buf, sink, stream=None):
     _check("medusa_hbm_read_probe", st)
 
 
+def medusa_clock_probe(ticks, sink, stream=None):
+    """ticks: int64 [2] device tensor (shader clock ticks, 100 MHz ticks); sink: int32 [1]."""
+    torch = _torch()
+    st = lib().medusa_clock_probe(_ptr(ticks, torch.int64, "ticks"), _ptr(sink, torch.int32, "sink"),
+                                  _stream(stream))
+    _check("medusa_clock_probe", st)
+
+
 def medusa_proxy_workspace(dt, M, H, Hq, Hkv, d) -> int:
     return int(lib().medusa_proxy_workspace(_dt(dt), M, H, Hq, Hkv, d))
 

@@ -76,6 +76,47 @@ def close_verify_logits(name: str, got, want, nh_got, nh_want, w_lm, dtype: str,
     return int((diff > 0).sum())
 
 
+def close_node_hidden(name: str, got, want, o_got, o_want, x, wo, dtype: str,
+                      rtol: float = RTOL, atol: float = ATOL) -> int:
+    """Node hidden states rnd(x + Wo o) against the oracle, in two parts, like the
+    verification logits: the attention output o is a bf16 activation, and each element
+    the device rounds to the neighbouring bf16 value of the oracle's (a flip within o's own
+    tolerance, which is checked) moves row i of the output projection by exactly
+    delta * Wo[i, j].
+
+    1. the kernel: the device's node hidden states against the oracle's output projection
+       of the device's own o (same x), at atol + rtol * |ref|;
+    2. the chain: |gpu - oracle| <= atol + rtol * |oracle| + sum_j |o_gpu,j - o_oracle,j|
+       * |Wo[i, j]|.
+
+    Shapes: got/want/x [..., H]; o_got/o_want [..., Hq, d] with the same leading axes.
+    Returns the number of flipped o elements."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    lead = got.shape[:-1]
+    H = got.shape[-1]
+    og = np.asarray(o_got, dtype=np.float64).reshape(-1, int(np.prod(np.shape(o_got)[len(lead):])))
+    ow = np.asarray(o_want, dtype=np.float64).reshape(og.shape)
+    xf = np.asarray(x, dtype=np.float64).reshape(-1, H)
+    own = oracle.proxy_out(xf.reshape(1, -1, H), og.reshape(1, og.shape[0], 1, -1), wo,
+                           dtype).reshape(got.shape)
+    close(f"{name} (oracle output projection of the device's o)", got, own, rtol, atol)
+    diff = np.abs(og - ow)
+    cols = np.nonzero(diff.max(axis=0) > 0)[0]
+    term = np.zeros((og.shape[0], H))
+    if len(cols):
+        wc = np.abs(oracle.as_f64(np.ascontiguousarray(wo[:, cols]), dtype))   # [H, c]
+        term = diff[:, cols] @ wc.T
+    term = term.reshape(got.shape)
+    excess = np.abs(got - want) - (atol + rtol * np.abs(want) + term * (1 + 1e-6))
+    if excess.size and excess.max() > 0:
+        i = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        raise AssertionError(f"{name}: |gpu-oracle| exceeds {atol}+{rtol}*|oracle| + flip term "
+                             f"at {i}: gpu {got[i]} oracle {want[i]} flip term {term[i]} "
+                             f"({int((excess > 0).sum())} of {excess.size} elements)")
+    return int((diff > 0).sum())
+
+
 def exact(name: str, got, want) -> None:
     got = np.asarray(got, dtype=np.int64)
     want = np.asarray(want, dtype=np.int64)
@@ -180,7 +221,8 @@ def compare_step(inp, got: dict, ref: "oracle.StepResult", check_logits: bool = 
         lambda: close("k_tree", got["k_tree"], ref.k),
         lambda: close("v_tree", got["v_tree"], ref.v),
         lambda: close("o", got["o"], ref.o),
-        lambda: close("node_hidden", got["node_hidden"], ref.node_hidden),
+        lambda: close_node_hidden("node_hidden", got["node_hidden"], ref.node_hidden, got["o"],
+                                  ref.o, ref.x, inp.wo, inp.dtype),
     ]
     if check_u:
         checks.append(lambda: close("u", got["u"], ref.u))

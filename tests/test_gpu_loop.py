@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import close, exact, oracle_plan, planted, say
+from tests.gpu_util import close_node_hidden, close, exact, oracle_plan, planted, say
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +70,7 @@ def test_advance_matches_oracle(dev, cfg, seed):
     st.run(bootstrap_root=True)
     k_tree = st.k_tree.clone()
     nh = st.node_hidden.clone()
+    o_dev = st.o.float().cpu().numpy()
     over = torch.full((inp.cfg.B,), -1, dtype=torch.int32, device=dev)
     st.advance(overflow=over)
     torch.cuda.synchronize()
@@ -90,7 +91,10 @@ def test_advance_matches_oracle(dev, cfg, seed):
         # and they equal the oracle's rows within the activation tolerance
         close(f"seq {b} appended k", kc[b, L: L + a + 1].float().cpu().numpy(),
               oracle.as_f64(nxt.k_cache[b, L: L + a + 1], inp.dtype))
-        close(f"seq {b} next h", w["h"][b].float().cpu().numpy(), oracle.as_f64(nxt.h[b], inp.dtype))
+        i_star = path[a]
+        close_node_hidden(f"seq {b} next h", w["h"][b].float().cpu().numpy(),
+                          oracle.as_f64(nxt.h[b], inp.dtype), o_dev[b, i_star], res.o[b, i_star],
+                          res.x[b, i_star], inp.wo, inp.dtype)
 
 
 def test_advance_overflow_changes_nothing(dev):

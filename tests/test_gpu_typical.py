@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import close, close_verify_logits, exact, oracle_plan, planted, run_gpu, say
+from tests.gpu_util import (close, close_node_hidden, close_verify_logits, exact, oracle_plan,
+                            planted, run_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,15 +46,37 @@ def dev():
     return torch.device("cuda:0")
 
 
+def _close_calls(plan, prob, tau):
+    """Candidates whose probability sits within the tolerance of their parent's threshold."""
+    B, N = prob.shape
+    n = 0
+    for bb in range(B):
+        for i in range(1, N):
+            par = int(plan.parent[i])
+            if abs(prob[bb, i] - tau[bb, par]) <= PROB_RTOL * max(prob[bb, i], tau[bb, par]):
+                n += 1
+    return n
+
+
 def _check_typical(inp, got, ref, plan, T, eps, delta, sure=False):
+    """Typical acceptance, stage by stage: the node hidden states against the oracle (with
+    the flip term of their bf16 input o); the probabilities and thresholds against the
+    oracle's rule applied to the oracle's lm_head of the device's own node hidden states
+    (lm_head itself is checked in the step tests); the accept results against the device's
+    own walk, and against the oracle's decisions when none sits within tolerance of its
+    threshold."""
     a, nodes, toks, prob, tau = oracle.typical_accept(plan, ref.tokens, ref.logits,
                                                       ref.node_argmax, T, eps, delta)
     exact("root_ids", got["root_ids"], ref.root)
     exact("node_tokens", got["node_tokens"], ref.tokens)
     exact("node_argmax", got["node_argmax"], ref.node_argmax)
-    close("node_hidden", got["node_hidden"], ref.node_hidden)
-    close("node_prob", got["node_prob"], prob, rtol=PROB_RTOL, atol=PROB_ATOL)
-    close("node_tau", got["node_tau"], tau, rtol=PROB_RTOL, atol=PROB_ATOL)
+    close_node_hidden("node_hidden", got["node_hidden"], ref.node_hidden, got["o"], ref.o, ref.x,
+                      inp.wo, inp.dtype)
+    own_logits = oracle.verify(np.asarray(got["node_hidden"], np.float64), inp.w_lm, inp.dtype)[0]
+    a_own, nodes_own, toks_own, prob_own, tau_own = oracle.typical_accept(
+        plan, ref.tokens, own_logits, ref.node_argmax, T, eps, delta)
+    close("node_prob", got["node_prob"], prob_own, rtol=PROB_RTOL, atol=PROB_ATOL)
+    close("node_tau", got["node_tau"], tau_own, rtol=PROB_RTOL, atol=PROB_ATOL)
     # the device's walk over its own probabilities and thresholds
     ga, gn, gt = oracle.typical_branch(plan, got["node_tokens"], got["node_argmax"],
                                        got["node_prob"].astype(np.float64),
@@ -61,20 +84,16 @@ def _check_typical(inp, got, ref, plan, T, eps, delta, sure=False):
     exact("accept_len (device rule)", got["accept_len"], ga)
     exact("accept_nodes (device rule)", got["accept_nodes"], gn)
     exact("accept_tokens (device rule)", got["accept_tokens"], gt)
-    # and the oracle's decisions, where none is within tolerance of its threshold
-    B, N = ref.tokens.shape
-    close_calls = 0
-    for b in range(B):
-        for i in range(1, N):
-            par = int(plan.parent[i])
-            if abs(prob[b, i] - tau[b, par]) <= PROB_RTOL * max(prob[b, i], tau[b, par]):
-                close_calls += 1
+    # and the oracle's decisions, on both sets of logits, where none is within tolerance
+    close_calls = _close_calls(plan, prob, tau) + _close_calls(plan, prob_own, tau_own)
     if sure:
         assert close_calls == 0, f"{close_calls} oracle decisions sit within tolerance"
     if close_calls == 0:
-        exact("accept_len", got["accept_len"], a)
-        exact("accept_nodes", got["accept_nodes"], nodes)
-        exact("accept_tokens", got["accept_tokens"], toks)
+        for name, g, o1, o2 in (("accept_len", got["accept_len"], a, a_own),
+                                ("accept_nodes", got["accept_nodes"], nodes, nodes_own),
+                                ("accept_tokens", got["accept_tokens"], toks, toks_own)):
+            exact(name, g, o1)
+            exact(name + " (oracle on the device's node_hidden)", g, o2)
     say(f"    accept {got['accept_len'].tolist()} (oracle {a.tolist()}), "
         f"{close_calls} decisions within tolerance of the threshold")
 
