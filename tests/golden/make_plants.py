@@ -48,6 +48,8 @@ def ranks_for(cfg_name: str, seed: int, accept):
 
 
 def main(argv):
+    import faulthandler
+    faulthandler.dump_traceback_later(900, repeat=True)   # where a long plant spends its time
     cfg = argv[1]
     if "--accept" in argv:
         i = argv.index("--accept")

@@ -246,6 +246,7 @@ def plant(cfg, seed: int, max_attempts: int = 12, verbose: bool = False,
             log(f"attempt {attempt}: tied greedy step")
             continue
         ok = False
+        fixes: Dict[tuple, int] = {}
         for it in range(30):
             if not _fix_heads(ed, inp, plan, chain):
                 break
@@ -274,7 +275,14 @@ def plant(cfg, seed: int, max_attempts: int = 12, verbose: bool = False,
                 else:
                     x, lg = res.node_hidden[b, dc.where[1]], res.logits[b, dc.where[1]]
                 top2 = oracle.topk(lg, 2)
-                ed.move("w_lm", -1, int(top2[0]), x, float(lg[top2[1]]) + SPACING)
+                # raise the winner; a decision that is still close after that (another
+                # decision's fix moved it back) gets its runner-up pushed down as well
+                n_fix = fixes.get((dc.kind, dc.where), 0)
+                fixes[(dc.kind, dc.where)] = n_fix + 1
+                if n_fix % 2 == 0:
+                    ed.move("w_lm", -1, int(top2[0]), x, float(lg[top2[1]]) + SPACING)
+                else:
+                    ed.move("w_lm", -1, int(top2[1]), x, float(lg[top2[0]]) - SPACING)
         if not ok:
             log(f"attempt {attempt}: could not open every margin")
             continue

@@ -103,3 +103,36 @@ def test_mean_accept_matches_closed_form():
     vals = np.array(vals, dtype=np.float64)
     se = vals.std() / np.sqrt(len(vals))
     assert abs(vals.mean() - expect) < 4 * se, (vals.mean(), expect, se)
+
+
+FULL_SHAPES = ("8b", "mid", "dense")     # batched 70B: lengths 0-4 so far
+
+
+@pytest.mark.parametrize("cfg_name", FULL_SHAPES)
+def test_stored_plants_cover_every_accept_length(cfg_name):
+    """The stored full-size plants reach every accepted length 0..D of their tree
+    (D = the tree's depth), and each patch's recorded length is the one its planted ranks
+    give under the tree walk.  (The margins of these patches are asserted when they are
+    written, and every GPU full-size test checks the step against the oracle.)"""
+    cfg = CONFIGS[cfg_name]
+    seen = set()
+    for fname in sorted(os.listdir(PLANTS)):
+        if not (fname.endswith(".json") and fname[:-5].rsplit("_s", 1)[0] == cfg_name):
+            continue
+        seed = int(fname[:-5].rsplit("_s", 1)[1])
+        with open(os.path.join(PLANTS, fname)) as f:
+            patch = json.load(f)
+        assert patch["config"] == cfg_name and patch["seed"] == seed
+        assert patch["thr"] >= 1e-2
+        acc = accuracy_table(cfg, seed)
+        plan = planting.plan_for(cfg, acc)
+        if "plant_rank" in patch:
+            ranks = np.asarray(patch["plant_rank"], dtype=np.int32)
+        else:
+            from synth.gen import _plant_ranks
+            ranks = _plant_ranks(cfg, seed, acc)
+        want = [planting.expected_accept_len(plan, ranks[b]) for b in range(cfg.B)]
+        assert patch["accept_len"] == want, (fname, patch["accept_len"], want)
+        seen.update(want)
+        depth = plan.max_depth
+    assert seen == set(range(depth + 1)), (cfg_name, sorted(seen), depth)
