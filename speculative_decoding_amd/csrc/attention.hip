@@ -5,12 +5,15 @@
 // Work split.  For one sequence b and one kv head g the query rows are the N*G
 // (node, query head) pairs of that group; they share every key, so they are the M side of
 // two MFMA contractions (scores and the value sum).  A workgroup takes a block of query
-// rows and one key range: a chunk of the prefix, or the tree keys.  Partial (max, sum,
-// unnormalised output) per key range go to the workspace; a second kernel combines them.
-// The ancestor mask is one 64-bit word per (node, 64 keys).
+// rows and one key range: a chunk of the prefix, possibly with the tree keys.  Partial
+// (max, sum, unnormalised output) per key range go to the workspace; a second kernel
+// combines them.  The ancestor mask is one 64-bit word per (node, 64 keys).
 //
-// bf16 (attn_tile_kernel): 32 x 32 x 16 MFMA tiles, each wave owning 32 or 64 query rows,
-// so every K or V fragment read from LDS feeds one or two MFMAs of 32 x 32 outputs.  Scores
+// bf16 (attn_tile_kernel): the workgroups of a (kv head, query-row block) share out the
+// keys of all sequences by their actual prefix lengths (attn_find_slot), so ragged batches
+// fill one round of the chip instead of reserving slots for the longest possible prefix.
+// 32 x 32 x 16 MFMA tiles, one 32-row query tile per wave, four or eight waves sharing the
+// K/V blocks staged in LDS.  Scores
 // are computed transposed, S^T = K Q^T: a lane owns one query column of each 32-row tile
 // (shared with the lane 32 apart) and 16 keys of every 32.  The value sum O^T = V^T P^T
 // takes P^T straight from the score registers as fp16 and V^T from LDS as fp16: bf16 values
@@ -32,7 +35,7 @@ namespace medusa {
 namespace {
 
 constexpr int kThreads = 256;     // the combine kernel
-// Waves (16 query rows each) per attention workgroup: the K/V blocks staged in LDS are
+// fp32 kernel: waves (16 query rows each) per workgroup: the K/V blocks staged in LDS are
 // shared by all of them, so more waves mean fewer passes of the same keys through each CU.
 // Measured: 8 waves help at 512 and more query rows per kv head (dense 256-node tree 105 ->
 // 102 us, batched 70B 316 -> 300 us) and cost 3 us at 256 (the 8B tree: 22.5 -> 25.5 us),
@@ -81,9 +84,135 @@ struct AttnArgs {
     const void* v_cache;
     const int32_t* prefix_lens;
     void* out;
-    float* ws_o;    // [B][Hkv][slots][rows][d]
-    float* ws_ml;   // [B][Hkv][slots][rows][2]
+    float* ws_o;    // fp32 kernel: [B][Hkv][slots][rows][d]; bf16: [workgroup][rows][d]
+    float* ws_ml;   // the same rows x (running maximum, sum)
+    int* ws_plan;   // bf16: [B] first workgroup slot of each sequence, then [B] slot counts
 };
+
+// ---- the bf16 kernel's split of the keys ----
+// The workgroups of one (kv head, query-row block) unit, sh.n_slots of them, share out the
+// keys of all sequences: sequence b takes n_b consecutive slots, ceil(L_b / C) prefix
+// chunks of C keys and the tree keys, which join the last chunk when they fit into its
+// spare room and take a slot of their own otherwise (an empty prefix: one slot, the tree).
+// C is the smallest multiple of 64, at least sh.chunk, for which the slots of all
+// sequences fit the unit's workgroups; the longest slot bounds the kernel's time.
+__device__ __forceinline__ int attn_slots_of(int L, int N, int C) {
+    const int np = (L + C - 1) / C;
+    return np == 0 ? 1 : np + (L + N > np * C ? 1 : 0);
+}
+// Whole-wave sum / maximum on DPP row steps and four lane reads; every lane gets it.
+__device__ __forceinline__ int wave_sum_int(int v) {
+    v += dpp_i<kDppXor1>(v);
+    v += dpp_i<kDppXor2>(v);
+    v += dpp_i<kDppHalfMirror>(v);
+    v += dpp_i<kDppMirror>(v);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+    v = max(v, dpp_i<kDppXor1>(v));
+    v = max(v, dpp_i<kDppXor2>(v));
+    v = max(v, dpp_i<kDppHalfMirror>(v));
+    v = max(v, dpp_i<kDppMirror>(v));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_scan_int(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const int u = __shfl_up(v, m, 64);
+        if (lane >= m) v += u;
+    }
+    return v;
+}
+// Hardware block h runs on XCD h % 8 as that XCD's (h / 8)-th block.  Group j = (slot,
+// kv head), slot-major, goes to XCD j % 8 with its nq row blocks in consecutive places
+// there, so they share one L2 for the keys they read; the groups start in order, so the
+// low slots, which hold work whenever the sequences need them, go first to distinct CUs.
+__device__ __forceinline__ void attn_block_map(int h, int groups, int nq, int& grp, int& qb) {
+    const int full = groups & ~7;              // groups in whole rounds of the 8 XCDs
+    if (h < full * nq) {
+        const int x = h & 7, k = h >> 3;
+        grp = (k / nq) * 8 + x;
+        qb = k % nq;
+    } else {
+        const int t = h - full * nq;
+        grp = full + t / nq;
+        qb = t % nq;
+    }
+}
+struct AttnSlot {
+    int b;            // sequence; -1: an idle workgroup
+    int n;            // the sequence's slot count
+    int p_begin, p_end;
+    bool with_tree;
+};
+// Called by every lane of a wave; the result is the same in all lanes.  `plan_out`, when
+// not null, receives every sequence's first slot and slot count.
+__device__ AttnSlot attn_find_slot(const int32_t* lens, int B, int Lcap, int N, int S, int cmin,
+                                   int slot, int* plan_out) {
+    const int lane = threadIdx.x & 63;
+    // lane l holds sequence b0 + l; up to 64 sequences the lengths stay in registers
+    const int L0 = lane < B ? min(max(lens[lane], 0), Lcap) : 0;
+    auto len_of = [&](int b0) {
+        if (B <= 64) return L0;
+        return b0 + lane < B ? min(max(lens[b0 + lane], 0), Lcap) : 0;
+    };
+    auto total_slots = [&](int C) {
+        int t = 0;
+        for (int b0 = 0; b0 < B; b0 += 64) t += wave_sum_int(b0 + lane < B ? attn_slots_of(len_of(b0), N, C) : 0);
+        return t;
+    };
+    int sumw = 0, maxw = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int w = b0 + lane < B ? len_of(b0) + N : 0;
+        sumw += wave_sum_int(w);
+        maxw = max(maxw, wave_max_int(w));
+    }
+    // C >= sum(W) / S is necessary (a sequence of W keys needs W / C slots or more), and
+    // with one sequence sufficient; `hi` (one slot per sequence, B <= S) always fits.
+    int lo = max(max(1, cmin / 64), (sumw + 64 * S - 1) / (64 * S));
+    int hi = max(lo, (maxw + 63) / 64);
+    if (total_slots(64 * lo) <= S) {
+        hi = lo;
+    } else {
+        ++lo;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (total_slots(64 * mid) <= S) hi = mid;
+            else lo = mid + 1;
+        }
+    }
+    const int C = 64 * hi;
+    AttnSlot r{-1, 0, 0, 0, false};
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int b = b0 + lane;
+        const int L = len_of(b0);
+        const int n = b < B ? attn_slots_of(L, N, C) : 0;
+        const int off = carry + wave_scan_int(n) - n;
+        if (plan_out && b < B) {
+            plan_out[b] = off;
+            plan_out[B + b] = n;
+        }
+        const unsigned long long hit = __ballot(b < B && off <= slot && slot < off + n);
+        if (hit) {
+            const int src = __ffsll((long long)hit) - 1;
+            const int j = slot - __shfl(off, src, 64);
+            const int nb = __shfl(n, src, 64);
+            const int Lb = __shfl(L, src, 64);
+            r.b = b0 + src;
+            r.n = nb;
+            r.p_begin = min(j * C, Lb);      // the tree's own slot: an empty prefix range
+            r.p_end = min((j + 1) * C, Lb);
+            r.with_tree = j == nb - 1;
+        }
+        carry = __shfl(off + n, 63, 64);        // off already counts the earlier chunks
+    }
+    return r;
+}
 
 template <typename T> struct Vt4;
 template <> struct Vt4<float> {
@@ -404,31 +533,41 @@ __device__ __noinline__ void attn_rows_fp32(const bf16_t* q, const bf16_t* kpre,
 }
 
 // Compile-time tuning overrides (0: chosen from the shape).
-#ifndef MEDUSA_ATTN_R
-#define MEDUSA_ATTN_R 0
+#ifndef MEDUSA_ATTN_WGS
+#define MEDUSA_ATTN_WGS 0          // bf16: workgroups per launch (0: one round of the chip)
 #endif
-#ifndef MEDUSA_ATTN_SPLITS
-#define MEDUSA_ATTN_SPLITS 0
+#ifndef MEDUSA_ATTN_MERGE_J
+#define MEDUSA_ATTN_MERGE_J 4      // bf16 merge: slots whose loads are in flight together
+#endif
+#ifndef MEDUSA_ATTN_MIN_CHUNK
+#define MEDUSA_ATTN_MIN_CHUNK 256  // bf16: fewest prefix keys per chunk
 #endif
 #ifndef MEDUSA_ATTN_PRIO
 #define MEDUSA_ATTN_PRIO 0    // raise the wave priority around its MFMA runs
 #endif
 
-constexpr int kTileWaves = 4;
-constexpr int kTileThreads = kTileWaves * 64;
+
+#ifndef MEDUSA_ATTN_W
+#define MEDUSA_ATTN_W 0       // waves per workgroup (0: chosen from the shape)
+#endif
+
 constexpr int kTileKeys = 64;       // keys per LDS block
 constexpr float kLazyMax = 8.f;     // rescale once a row maximum grows by more than 2^8
 
-// R: 32-row query tiles per wave (1 or 2); D: head dim (64 or 128).
-template <int D, int R>
-__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(R == 1 ? 2 : 1)))
+// D: head dim (64 or 128); NW: waves per workgroup (4 or 8), one 32-row query tile each.
+// The NW waves share every K / V block staged in LDS, so eight waves halve the staging per
+// query row; they need 256 query rows per kv head to fill their tiles.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_tile_kernel(const AttnArgs a) {
+    constexpr int R = 1;                 // 32-row query tiles per wave
+    constexpr int kTileThreads = NW * 64;
     constexpr int KB = kTileKeys;
     constexpr int KP = D + 8;            // K row pitch: rows 4 banks apart, 8 rows cover 32
     constexpr int VP = KB + 8;           // V^T row pitch: rows 4 banks apart, 8 rows cover 32
     constexpr int KS = D / 16;           // 16-deep steps over the head dim
     constexpr int DT = D / 32;           // 32-row tiles of O^T over the head dim
-    constexpr int ROWS = 32 * R * kTileWaves;
+    constexpr int ROWS = 32 * R * NW;
     constexpr int KVEC = KB * D / 8;                 // 16-byte K pieces per block
     constexpr int KPT = KVEC / kTileThreads;         // ... per thread
     constexpr int VUNITS = (KB / 4) * (D / 8);       // V units: 4 keys x 8 head-dim elements
@@ -439,24 +578,20 @@ void attn_tile_kernel(const AttnArgs a) {
 
     const AttnShape& sh = a.s;
     const int n_slots = sh.n_slots;
-    const int nblocks = sh.B * sh.Hkv * n_slots * sh.n_qblocks;
-    int bid = xcd_logical_block(blockIdx.x, nblocks);
-    const int qb = bid % sh.n_qblocks;
-    bid /= sh.n_qblocks;
-    const int slot = bid % n_slots;
-    bid /= n_slots;
-    const int g = bid % sh.Hkv;
-    const int b = bid / sh.Hkv;
-
-    // the prefix length is uniform: keep it (and every loop bound) in scalar registers.
-    // Slot s takes prefix keys [s chunk, (s+1) chunk) up to L; the last live slot (slot 0
-    // for an empty prefix) also takes the tree keys.
-    const int L = min(max(__builtin_amdgcn_readfirstlane(a.prefix_lens[b]), 0), sh.Lcap);
-    const int last = L > 0 ? (L - 1) / sh.chunk : 0;
-    if (slot > last) return;           // empty prefix chunk: the combine skips this slot
-    const int p_begin = slot * sh.chunk;
-    const int p_end = min(L, p_begin + sh.chunk);
-    const bool with_tree = slot == last;
+    int grp, qb;
+    attn_block_map(blockIdx.x, n_slots * sh.Hkv, sh.n_qblocks, grp, qb);
+    const int slot = grp / sh.Hkv;
+    const int g = grp % sh.Hkv;
+    const int bid = (g * n_slots + slot) * sh.n_qblocks + qb;     // this workgroup's partial block
+    const AttnSlot as = attn_find_slot(a.prefix_lens, sh.B, sh.Lcap, sh.N, n_slots, sh.chunk, slot,
+                                       bid == 0 && threadIdx.x < 64 ? a.ws_plan : nullptr);
+    // uniform values: keep them (and every loop bound) in scalar registers
+    const int b = __builtin_amdgcn_readfirstlane(as.b);
+    if (b < 0) return;                 // more workgroups than slots
+    const int n_seq_slots = __builtin_amdgcn_readfirstlane(as.n);
+    const int p_begin = __builtin_amdgcn_readfirstlane(as.p_begin);
+    const int p_end = __builtin_amdgcn_readfirstlane(as.p_end);
+    const bool with_tree = __builtin_amdgcn_readfirstlane((int)as.with_tree) != 0;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -707,7 +842,8 @@ void attn_tile_kernel(const AttnArgs a) {
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) bad |= !__builtin_isfinite(o[t][dt][v]);
-    const long long slot_base = (((long long)b * sh.Hkv + g) * n_slots + slot) * sh.rows;
+    // this workgroup's partial rows: row r of the kv head at slot_base + r
+    const long long slot_base = ((long long)bid - qb) * ROWS;
     bf16_t* const out = static_cast<bf16_t*>(a.out);
     const bool fallback = __syncthreads_or(bad);
     if (fallback)
@@ -716,9 +852,10 @@ void attn_tile_kernel(const AttnArgs a) {
                           a.ws_ml + slot_base * 2, sh.rows, sh.N, sh.G, sh.Hq, g, kstride,
                           a.scale_log2, qb * ROWS, ROWS, p_begin, p_end, with_tree);
 
-    // The only live slot of its row block writes the attention output straight from its
+    // The only slot of its sequence writes the attention output straight from its
     // registers.
-    if (last == 0 && !fallback) {
+    const bool only = n_seq_slots == 1;
+    if (only && !fallback) {
 #pragma unroll
         for (int t = 0; t < R; ++t) {
             const float inv = 1.f / sum_xor32(l_sum[t]);
@@ -736,8 +873,8 @@ void attn_tile_kernel(const AttnArgs a) {
         return;
     }
 
-    // After the fp32 recomputation, the only live slot normalises the partial it wrote.
-    if (last == 0) {
+    // After the fp32 recomputation, the only slot normalises the partial it wrote.
+    if (only) {
         __syncthreads();
         for (int i = tid; i < ROWS * (D / 8); i += kTileThreads) {
             const int r = qb * ROWS + i / (D / 8);
@@ -779,13 +916,13 @@ void attn_tile_kernel(const AttnArgs a) {
     }
 }
 
-// bf16: merge the partials of the row blocks that have more than one live slot (a row
-// block whose only live slot wrote its output directly is skipped).  Sixteen threads per
-// query row, eight head-dim elements each; every slot's loads are issued before they are
-// used.
+// bf16: merge the partials of the sequences that took more than one slot (a sequence with
+// one slot had its output written directly).  Sixteen threads per query row, eight
+// head-dim elements each; MEDUSA_ATTN_MERGE_J slots' loads are issued before any is used.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
     constexpr int TPR = D / 8;                       // threads per row
+    constexpr int MAXJ = MEDUSA_ATTN_MERGE_J;        // slots per pass
     const AttnShape& sh = a.s;
     const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long total = (long long)sh.B * sh.Hkv * sh.rows * TPR;
@@ -796,20 +933,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
     const int bg = (int)(row_id / sh.rows);
     const int b = bg / sh.Hkv;
     const int g = bg % sh.Hkv;
-    const int L = min(max(a.prefix_lens[b], 0), sh.Lcap);
-    const int last = L > 0 ? (L - 1) / sh.chunk : 0;
-    if (last == 0) return;
-    const long long base0 = (long long)bg * sh.n_slots * sh.rows + r;
-    // one pass with a running maximum, four slots' loads in flight at a time
+    const int n = a.ws_plan[sh.B + b];               // the sequence's slots
+    if (n <= 1) return;                              // written directly by its only slot
+    const int first = a.ws_plan[b];
+    const int per = 32 * sh.waves;                   // query rows per workgroup
+    const int qb = r / per;
+    // slot j's partial row: workgroup ((g n_slots + first + j) n_qblocks + qb), row r % per
+    const long long base0 = (((long long)g * sh.n_slots + first) * sh.n_qblocks + qb) * per + r % per;
+    const long long step = (long long)sh.n_qblocks * per;
+    // one pass with a running maximum
     float mx = -INFINITY, den = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 <= last; s0 += 4) {
-        float ms[4], ls[4];
-        floatx4 v0[4], v1[4];
+    for (int s0 = 0; s0 < n; s0 += MAXJ) {
+        float ms[MAXJ], ls[MAXJ];
+        floatx4 v0[MAXJ], v1[MAXJ];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int sl = min(s0 + u, last);
-            const long long bs = base0 + (long long)sl * sh.rows;
+        for (int u = 0; u < MAXJ; ++u) {
+            const int sl = min(s0 + u, n - 1);
+            const long long bs = base0 + (long long)sl * step;
             ms[u] = a.ws_ml[bs * 2];
             ls[u] = a.ws_ml[bs * 2 + 1];
             const floatx4* src = reinterpret_cast<const floatx4*>(a.ws_o + bs * D + part * 8);
@@ -817,8 +958,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
             v1[u] = src[1];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (s0 + u > last || ms[u] == -INFINITY) continue;
+        for (int u = 0; u < MAXJ; ++u) {
+            if (s0 + u >= n || ms[u] == -INFINITY) continue;
             const float m_new = fmaxf(mx, ms[u]);
             const float alpha = mx == -INFINITY ? 0.f : exp2f(mx - m_new);
             const float w = exp2f(ms[u] - m_new);
@@ -917,13 +1058,13 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnArgs a
 template <typename T, int D>
 hipError_t launch_td(const AttnArgs& a, hipStream_t stream) {
     const AttnShape& s = a.s;
-    const int nblocks = s.B * s.Hkv * s.n_slots * s.n_qblocks;
     if constexpr (std::is_same<T, bf16_t>::value) {
+        const int nblocks = s.Hkv * s.n_slots * s.n_qblocks;
         prof_begin("attn_partial", stream);
-        if (s.tile_r == 2)
-            hipLaunchKernelGGL((attn_tile_kernel<D, 2>), dim3(nblocks), dim3(kTileThreads), 0, stream, a);
+        if (s.waves == 8)
+            hipLaunchKernelGGL((attn_tile_kernel<D, 8>), dim3(nblocks), dim3(8 * 64), 0, stream, a);
         else
-            hipLaunchKernelGGL((attn_tile_kernel<D, 1>), dim3(nblocks), dim3(kTileThreads), 0, stream, a);
+            hipLaunchKernelGGL((attn_tile_kernel<D, 4>), dim3(nblocks), dim3(4 * 64), 0, stream, a);
         prof_end(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -934,6 +1075,7 @@ hipError_t launch_td(const AttnArgs& a, hipStream_t stream) {
         prof_end(stream);
         return hipGetLastError();
     } else {
+        const int nblocks = s.B * s.Hkv * s.n_slots * s.n_qblocks;
         prof_begin("attn_partial", stream);
         if (s.waves == kAttnWavesLarge)
             hipLaunchKernelGGL((attn_partial_kernel<T, D, kAttnWavesLarge>), dim3(nblocks),
@@ -959,61 +1101,62 @@ AttnShape attn_shape(medusa_dtype dt, int B, int N, int Hq, int Hkv, int d, int 
     s.B = B; s.N = N; s.Hq = Hq; s.Hkv = Hkv; s.d = d; s.Lcap = Lcap;
     s.G = Hq / Hkv;
     s.rows = N * s.G;
-    const int max_splits = Lcap > 0 ? (Lcap + kKeys - 1) / kKeys : 1;
-    int splits;
     if (dt == MEDUSA_BF16) {
-        // 32 x 32 tiles: two per wave once a kv head has 256 query rows (each K/V fragment
-        // then feeds two MFMAs), one below.  Prefix splits give about `target` workgroups.
+        // One 32-row query tile per wave.  Eight waves from 512 query rows per kv head
+        // (two or more blocks of 256 rows sharing every staged K/V block), four below.
+        // Measured (tile kernel, us, 4 -> 8 waves): dense tree 70.8 -> 58.9, batched 70B
+        // 152 -> 134, 8B shape (256 rows) 22.2 -> 26.5.
         s.tile_r = 1;
-#if MEDUSA_ATTN_R
-        s.tile_r = MEDUSA_ATTN_R;
+        s.waves = s.rows >= 512 ? 8 : 4;
+#if MEDUSA_ATTN_W
+        s.waves = MEDUSA_ATTN_W;
 #endif
-        s.waves = kTileWaves;
-        const int per = 32 * s.tile_r * kTileWaves;
+        const int per = 32 * s.waves;
         s.n_qblocks = (s.rows + per - 1) / per;
-        // prefix chunks: about 256 workgroups over the (sequence, kv head, row block)
-        // units, 4 to 12 chunks each, at least 256 keys per chunk.  Measured (us, tile +
-        // merge; best in brackets): 8B shape 16 units -> 12 chunks 22.4 + 10.7 [33.1; 4:
-        // 42, 8: 34.7]; 7B shape 32 -> 4 chunks 16.6 + 7.1 [6: 22.5]; dense tree 64 -> 4
-        // 70.0 + 8.1 [6: 75.7]; batched 70B 256 -> 4 147.9 + 10.4 [best]
-        const int base = B * Hkv * s.n_qblocks;
-        splits = (256 + base / 2) / base;
-        if (splits < 4) splits = 4;
-        if (splits > 12) splits = 12;
-        const int by_len = Lcap / 256;
-        if (splits > by_len) splits = by_len;
-#if MEDUSA_ATTN_SPLITS
-        splits = MEDUSA_ATTN_SPLITS;
-#endif
-    } else {
-        s.tile_r = 0;
-        s.waves = s.rows >= kAttnLargeRows ? kAttnWavesLarge : kAttnWavesSmall;
-        s.n_qblocks = (s.rows + 16 * s.waves - 1) / (16 * s.waves);
-        // Split the prefix so that (a) the partial outputs (rows * d fp32 per split) stay
-        // below about half the K/V bytes they summarise and (b) the grid still covers the
-        // chip when there are few (sequence, kv head, query block) triples: about 1024
-        // waves in flight.
-        splits = Lcap / (2 * s.rows);
-        const int base = B * Hkv * s.n_qblocks;
-        const int fill_blocks = 1024 / s.waves;
-        const int fill = (fill_blocks + base - 1) / base;
-        if (splits < fill) splits = fill;
+        // Workgroups per (kv head, row block) unit: as many as one round of the chip holds
+        // (one 8-wave or two 4-wave workgroups per CU), at least one per sequence; the
+        // kernel shares them out over the actual key counts (attn_find_slot).
+        const int wgs = MEDUSA_ATTN_WGS > 0 ? MEDUSA_ATTN_WGS : (s.waves == 8 ? 256 : 512);
+        const int units = Hkv * s.n_qblocks;
+        s.n_slots = wgs / units > B ? wgs / units : B;
+        s.chunk = MEDUSA_ATTN_MIN_CHUNK;
+        s.n_splits = 0;
+        s.tree_merged = 1;
+        return s;
     }
+    s.tile_r = 0;
+    s.waves = s.rows >= kAttnLargeRows ? kAttnWavesLarge : kAttnWavesSmall;
+    s.n_qblocks = (s.rows + 16 * s.waves - 1) / (16 * s.waves);
+    // Split the prefix so that (a) the partial outputs (rows * d fp32 per split) stay below
+    // about half the K/V bytes they summarise and (b) the grid still covers the chip when
+    // there are few (sequence, kv head, query block) triples: about 1024 waves in flight.
+    const int max_splits = Lcap > 0 ? (Lcap + kKeys - 1) / kKeys : 1;
+    int splits = Lcap / (2 * s.rows);
+    const int base = B * Hkv * s.n_qblocks;
+    const int fill_blocks = 1024 / s.waves;
+    const int fill = (fill_blocks + base - 1) / base;
+    if (splits < fill) splits = fill;
     if (splits < 1) splits = 1;
     if (splits > max_splits) splits = max_splits;
     int chunk = Lcap > 0 ? (Lcap + splits - 1) / splits : kKeys;
     chunk = (chunk + kKeys - 1) / kKeys * kKeys;
     s.chunk = chunk;
     s.n_splits = Lcap > 0 ? (Lcap + chunk - 1) / chunk : 0;
-    s.tree_merged = dt == MEDUSA_BF16 ? 1 : 0;
-    s.n_slots = s.tree_merged ? (s.n_splits > 0 ? s.n_splits : 1) : s.n_splits + 1;
+    s.tree_merged = 0;
+    s.n_slots = s.n_splits + 1;
     return s;
 }
 
+// Partial rows of the workspace: fp32 kernel [B][Hkv][slots][rows]; bf16 kernel one block
+// of 32 * waves rows per workgroup.
+static size_t attn_partial_rows(const AttnShape& s) {
+    if (s.tile_r > 0) return (size_t)s.Hkv * s.n_slots * s.n_qblocks * (32 * s.waves);
+    return (size_t)s.B * s.Hkv * s.n_slots * s.rows;
+}
+
 size_t attn_workspace_bytes(const AttnShape& s) {
-    const size_t slots = (size_t)s.n_slots;
-    const size_t rows = (size_t)s.B * s.Hkv * slots * s.rows;
-    return rows * (size_t)s.d * sizeof(float) + rows * 2 * sizeof(float) + 256;
+    const size_t rows = attn_partial_rows(s);
+    return rows * (size_t)s.d * sizeof(float) + rows * 2 * sizeof(float) + (size_t)s.B * 2 * sizeof(int) + 256;
 }
 
 hipError_t attention_launch(medusa_dtype dt, const AttnShape& s, const DevicePlan& plan, float scale,
@@ -1027,10 +1170,10 @@ hipError_t attention_launch(medusa_dtype dt, const AttnShape& s, const DevicePla
     a.q = q; a.k_tree = k_tree; a.v_tree = v_tree; a.k_cache = k_cache; a.v_cache = v_cache;
     a.prefix_lens = prefix_lens;
     a.out = out;
-    const size_t slots = (size_t)s.n_slots;
-    const size_t rows = (size_t)s.B * s.Hkv * slots * s.rows;
+    const size_t rows = attn_partial_rows(s);
     a.ws_o = static_cast<float*>(ws);
     a.ws_ml = a.ws_o + rows * s.d;
+    a.ws_plan = reinterpret_cast<int*>(a.ws_ml + rows * 2);
     if (dt == MEDUSA_BF16) {
         return s.d == 64 ? launch_td<bf16_t, 64>(a, stream) : launch_td<bf16_t, 128>(a, stream);
     }

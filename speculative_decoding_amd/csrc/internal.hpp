@@ -166,10 +166,12 @@ struct AttnShape {
     int waves;      // waves per workgroup
     int tile_r;     // bf16: 32-row query tiles per wave (1 or 2); fp32: 0 (16 rows per wave)
     int n_qblocks;  // query-row blocks per (sequence, kv head)
-    int chunk;      // prefix keys per split (multiple of 64)
-    int n_splits;   // prefix splits
-    int tree_merged;  // 1: the tree keys join the last live prefix chunk; 0: a slot of their own
-    int n_slots;    // partial results per (sequence, kv head, query row)
+    int chunk;      // fp32: prefix keys per split (multiple of 64); bf16: fewest keys per chunk
+    int n_splits;   // fp32: prefix splits
+    int tree_merged;  // 1 (bf16): the tree keys join a sequence's last chunk when they fit
+    int n_slots;    // fp32: partials per (sequence, kv head, query row); bf16: workgroups
+                    // per (kv head, query-row block), shared out over the sequences'
+                    // keys by the kernel
 };
 AttnShape attn_shape(medusa_dtype dt, int B, int N, int Hq, int Hkv, int d, int Lcap);
 size_t attn_workspace_bytes(const AttnShape& s);

@@ -3,13 +3,16 @@ oracle's tree_attention, element by element at 1e-3 + 2e-2 * |oracle| (glossary 
 Heads", section "Attention arborescente et acceptation": each node sees the prefix and its
 own ancestors).
 
-The bf16 kernel computes 32 x 32 tiles with one or two 32-row query tiles per wave; the
-shapes cover both (64 and fewer query rows per kv head take one, 256 and more take two),
-head dims 64 and 128, several query-row blocks with a ragged last one, empty and ragged
-prefixes, prefixes that end inside a 64-key block, several prefix splits, multi-head and
-grouped-query layouts, and the 8B-class shape.  Two cases put values beyond fp16's range
-(|v| up to 9e4) into the keys' values: the workgroups that meet them recompute their rows
-in fp32, and the result must still match."""
+The bf16 kernel computes 32 x 32 tiles, one 32-row query tile per wave.  Below 512 query
+rows per kv head a workgroup has four waves running in lock step; from 512 on it has eight,
+in two groups one phase apart (one group's softmax overlaps the other's matrix products),
+with the prefix keys fetched by bounds-checked buffer loads.  The workgroups of a (kv head,
+row block) are shared out over the sequences' actual key counts, so the shapes also take
+many ragged sequences and trees larger than a chunk.  The shapes cover both schedules, head dims 64 and 128, several query-row blocks with a ragged last one, empty,
+short (under one 32-key half) and ragged prefixes, prefixes that end inside a 64-key block
+or exactly on one, several prefix splits, multi-head and grouped-query layouts, and the
+8B-class shape.  Three cases put values beyond fp16's range (|v| up to 9e4) into the keys'
+values: the workgroups that meet them recompute their rows in fp32, and the result must still match."""
 import numpy as np
 import pytest
 
@@ -33,6 +36,19 @@ CASES = {
     "r2_d128_8b_shape": (1, ("sparse", (10, 5, 4, 3), 64), 32, 8, 128, (4096,), 4096, False),
     "r2_d128_fp16_overflow": (2, ("sparse", (10, 5, 4, 3), 64), 32, 8, 128, (700, 64), 768, True),
     "r1_d64_fp16_overflow": (3, ("sparse", (4, 3, 2), 16), 4, 1, 64, (0, 129, 300), 300, True),
+    # 512 and more query rows per kv head: eight waves, phase-shifted
+    "w8_d128_dense": (1, ("full", (4, 4, 4, 4)), 4, 1, 128, (1000,), 1024, False),
+    "w8_d64_two_seqs": (2, ("sparse", (10, 5, 4, 3), 64), 64, 8, 64, (0, 300), 320, False),
+    "w8_d128_short_prefix": (1, ("sparse", (10, 5, 4, 3), 64), 16, 2, 128, (20,), 64, False),
+    "w8_d128_exact_blocks": (2, ("sparse", (10, 5, 4, 3), 64), 16, 2, 128, (256, 129), 256, False),
+    "w8_d128_fp16_overflow": (2, ("sparse", (10, 5, 4, 3), 64), 64, 8, 128, (700, 64), 768, True),
+    # the key split shared out over ragged sequences: more sequences than one wave's lanes,
+    # a tree larger than the shortest chunk, and a batched grouped-query layout
+    "many_seqs_d64": (70, ("sparse", (4, 3, 2), 16), 4, 1, 64, tuple((37 * i) % 301 for i in range(70)), 300,
+                      False),
+    "w4_d128_tree341_short": (3, ("full", (4, 4, 4, 4)), 2, 2, 128, (0, 40, 700), 704, False),
+    "w8_batched_ragged": (8, ("sparse", (10, 5, 4, 3), 64), 16, 2, 128, (1006, 3549, 2810, 496, 1215, 1801, 1667,
+                                                                   2011), 3584, False),
 }
 
 
