@@ -1690,9 +1690,12 @@ hipError_t launch_t(GemmBatch& bt, hipStream_t stream) {
 // one block barrier per chunk orders them.  EPI_PARTIAL splits the contraction into
 // bt.ksplit slices and writes each slice's fp32 sums to part_val[slice][m][n] for the
 // finalize pass.  The LDS layout is tile_lds()'s.
+#ifndef MEDUSA_TILE_SWIZZLE
+#define MEDUSA_TILE_SWIZZLE 1
+#endif
 template <int WM, int WN, int MTW, int RTW, bool DB = false>
 constexpr size_t tile_lds() {
-    return (size_t)(16 * WM * MTW + 16 * WN * RTW) * (64 + 8) * 2 * (DB ? 2 : 1) +
+    return (size_t)(16 * WM * MTW + 16 * WN * RTW) * (MEDUSA_TILE_SWIZZLE ? 64 : 64 + 8) * 2 * (DB ? 2 : 1) +
            (size_t)WN * 16 * WM * MTW * 8;
 }
 
@@ -1702,7 +1705,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
     constexpr int TM = 16 * WM * MTW;           // input rows per tile
     constexpr int TN = 16 * WN * RTW;           // weight rows per tile
     constexpr int CH = 64;
-    constexpr int XP = CH + 8;
+    // LDS rows of CH elements (128 B, 8 units of 16 B) with no padding: unit u of row r is
+    // stored at unit u ^ ((r >> 1) & 7).  A 16-lane group's 16-byte stores then cover two
+    // whole rows (64 distinct banks) and its fragment reads (16 rows, one unit each) hit
+    // 16 distinct 4-bank groups; a padded pitch of 72 made every store pair overlap.
+    constexpr int XP = MEDUSA_TILE_SWIZZLE ? CH : CH + 8;
+    auto sw = [](int row, int col) __attribute__((always_inline)) {   // element offset in an LDS tile
+        return MEDUSA_TILE_SWIZZLE ? row * CH + ((((col >> 3) ^ (row >> 1)) & 7) << 3) : row * (CH + 8) + col;
+    };
     constexpr int LPR = CH / 8;                 // lanes per row per load instruction
     constexpr int RPI = NT / LPR;               // rows per workgroup load instruction
     constexpr int XL = TM / RPI;                // X loads per thread per chunk
@@ -1783,10 +1793,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
         bf16_t* ws = st + TM * XP;
 #pragma unroll
         for (int i = 0; i < XL; ++i)
-            *reinterpret_cast<u32x4*>(xs + (lrow + RPI * i) * XP + lcol) = xok[i] ? xr[i] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(xs + sw(lrow + RPI * i, lcol)) = xok[i] ? xr[i] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < WL; ++i)
-            *reinterpret_cast<u32x4*>(ws + (lrow + RPI * i) * XP + lcol) = wr[i];
+            *reinterpret_cast<u32x4*>(ws + sw(lrow + RPI * i, lcol)) = wr[i];
     };
 
     floatx4 acc[RTW][MTW];
@@ -1801,11 +1811,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
         for (int ks = 0; ks < CH; ks += 32) {
             Frag<bf16_t> wf[RTW];
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt) wf[rt].load(ws + (wn + rt * 16 + ln) * XP + ks + 8 * lg);
+            for (int rt = 0; rt < RTW; ++rt) wf[rt].load(ws + sw(wn + rt * 16 + ln, ks + 8 * lg));
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) {
                 Frag<bf16_t> xf;
-                xf.load(xs + (wm + mt * 16 + ln) * XP + ks + 8 * lg);
+                xf.load(xs + sw(wm + mt * 16 + ln, ks + 8 * lg));
 #pragma unroll
                 for (int rt = 0; rt < RTW; ++rt) mma(acc[rt][mt], xf, wf[rt]);
             }
@@ -1951,6 +1961,15 @@ int splitk_rt(int M) { return M <= 16 ? 2 : 1; }
 #ifndef MEDUSA_TILE_SPLIT
 #define MEDUSA_TILE_SPLIT 1
 #endif
+#ifndef MEDUSA_TILE_STORE_DB
+#define MEDUSA_TILE_STORE_DB 1
+#endif
+#ifndef MEDUSA_TILE_STORE_CFG
+#define MEDUSA_TILE_STORE_CFG 0
+#endif
+#ifndef MEDUSA_TILE_ARGMAX_CFG
+#define MEDUSA_TILE_ARGMAX_CFG 0
+#endif
 #ifndef MEDUSA_TILE_SPLIT_ROWS
 #define MEDUSA_TILE_SPLIT_ROWS 17
 #endif
@@ -1976,7 +1995,12 @@ hipError_t launch_splitk_rows(GemmBatch& bt, hipStream_t stream) {
 template <typename T>
 hipError_t launch_store(GemmBatch& bt, hipStream_t stream) {
     if (tile_store_eligible(sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, bt.M, bt.K))
-        return launch_tile<2, 2, kTileRtw, kTileRtw, EPI_STORE>(bt, stream);
+    {
+        constexpr bool DB = MEDUSA_TILE_STORE_DB != 0;
+        if (MEDUSA_TILE_STORE_CFG == 1) return launch_tile<2, 2, 2 * kTileRtw, kTileRtw, EPI_STORE, DB>(bt, stream);
+        if (MEDUSA_TILE_STORE_CFG == 2) return launch_tile<4, 2, kTileRtw, kTileRtw, EPI_STORE, DB>(bt, stream);
+        return launch_tile<2, 2, kTileRtw, kTileRtw, EPI_STORE, DB>(bt, stream);
+    }
     if (MEDUSA_SPLIT_ROWS && sizeof(T) == 2 && bt.K % (kSplitRowsChunk * kWaves) == 0) {
         if (bt.M <= 16) return launch_splitk_rows<1, 2>(bt, stream);
         if (bt.M <= 32) return launch_splitk_rows<2, 1>(bt, stream);
@@ -2109,8 +2133,12 @@ hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
     // gemm_rows_per_tile() reports, which sizes the partials and the grid
     static_assert(EPI != EPI_ARGMAX || 4 * 4 * 16 == NWV * 16 * RTW, "argmax tile rows");
     if (EPI == EPI_ARGMAX)
-        return bt.M <= 128 ? launch_tile<2, 4, 4, 4, EPI_ARGMAX>(bt, stream)
-                           : launch_tile<4, 4, 4, 4, EPI_ARGMAX, true>(bt, stream);
+    {
+        if (bt.M <= 128) return launch_tile<2, 4, 4, 4, EPI_ARGMAX>(bt, stream);
+        if (MEDUSA_TILE_ARGMAX_CFG == 1) return launch_tile<2, 4, 8, 4, EPI_ARGMAX, true>(bt, stream);
+        if (MEDUSA_TILE_ARGMAX_CFG == 2) return launch_tile<4, 2, 4, 8, EPI_ARGMAX, true>(bt, stream);
+        return launch_tile<4, 4, 4, 4, EPI_ARGMAX, true>(bt, stream);
+    }
     return launch_rowstream_t<8, EPI, RTW, PF, CH, NWV>(bt, stream);
 }
 
