@@ -767,9 +767,29 @@ constexpr int kRsRtwArgmax = MEDUSA_RS_RTW_ARGMAX;
 #ifndef MEDUSA_RS_RTW_SMALLV
 #define MEDUSA_RS_RTW_SMALLV 1
 #endif
+#ifndef MEDUSA_RS_PF_SMALLV
+#define MEDUSA_RS_PF_SMALLV 2       // small vocabulary: two chunks in flight (7B verify 73.5 -> 56.5 us)
+#endif
+#ifndef MEDUSA_RS_CHUNK_SMALLV
+#define MEDUSA_RS_CHUNK_SMALLV MEDUSA_RS_CHUNK
+#endif
 constexpr int kRsWavesSmallVocab = MEDUSA_RS_WAVES_SMALLV;
 constexpr int kRsRtwSmallVocab = MEDUSA_RS_RTW_SMALLV;
 bool rs_small_vocab(int M, int N) { return M <= 64 && N < MEDUSA_RS_SMALL_VOCAB; }
+
+#ifndef MEDUSA_RS_SWIZZLE
+#define MEDUSA_RS_SWIZZLE 1
+#endif
+#ifndef MEDUSA_TILE_SWIZZLE
+#define MEDUSA_TILE_SWIZZLE 1
+#endif
+// LDS tiles of 64-element rows (128 B, 8 units of 16 B) with no padding: unit u of row r is
+// stored at unit u ^ ((r >> 1) & 7).  A 16-lane group's 16-byte stores (two whole rows)
+// then cover 64 distinct banks and its MFMA fragment reads (16 rows, one unit each) hit 16
+// distinct 4-bank groups; a padded pitch of 72 made every pair of stored rows overlap.
+__device__ __forceinline__ int sw64(int row, int col) {
+    return row * 64 + ((((col >> 3) ^ (row >> 1)) & 7) << 3) + (col & 7);
+}
 
 template <int MT, int EPI, int RTW, int PF, int CH, int NWV>
 __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmBatch bt) {
@@ -777,7 +797,9 @@ __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmB
     constexpr int ROWS = 16 * RT;             // weight rows per wave
     constexpr int NWG = NWV * ROWS;
     constexpr int NTH = NWV * kWave;
-    constexpr int XP = CH + 8;                // LDS pitch of X rows and W tiles (elements)
+    constexpr bool SWZ = MEDUSA_RS_SWIZZLE && CH == 64;
+    constexpr int XP = SWZ ? CH : CH + 8;     // LDS pitch of X rows and W tiles (elements)
+    auto at = [](int row, int c) __attribute__((always_inline)) { return SWZ ? sw64(row, c) : row * XP + c; };
     constexpr int LPR = CH / 8;               // lanes per row in one load instruction
     constexpr int RPI = kWave / LPR;          // rows per load instruction
     constexpr int NI = ROWS / RPI;            // 16-byte loads per lane per chunk
@@ -839,7 +861,7 @@ __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmB
         const int idx = threadIdx.x + j * NTH;
         const int m = idx / VPR;
         const int c = idx - m * VPR;
-        xdst[j] = m < MT * 16 ? m * XP + c * 8 : MT * 16 * XP;
+        xdst[j] = m < MT * 16 ? at(m, c * 8) : MT * 16 * XP;
         long long r = 0;
         bool ok = m < Mb;
         if (ok) {
@@ -884,18 +906,18 @@ __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmB
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            *reinterpret_cast<u32x4*>(wtile + (RPI * i + half) * XP + col) = wr[p][i];
+            *reinterpret_cast<u32x4*>(wtile + at(RPI * i + half, col)) = wr[p][i];
         __syncthreads();
         load(p, c + PF);
 #pragma unroll
         for (int ks = 0; ks < CH; ks += 32) {
             Frag<bf16_t> wf[RT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) wf[rt].load(wtile + (rt * 16 + ln) * XP + ks + 8 * lg);
+            for (int rt = 0; rt < RT; ++rt) wf[rt].load(wtile + at(rt * 16 + ln, ks + 8 * lg));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 Frag<bf16_t> xf;       // rows past Mb hold zeros
-                xf.load(xs + (mt * 16 + ln) * XP + ks + 8 * lg);
+                xf.load(xs + at(mt * 16 + ln, ks + 8 * lg));
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) mma(acc[rt][mt], xf, wf[rt]);
             }
@@ -1690,9 +1712,6 @@ hipError_t launch_t(GemmBatch& bt, hipStream_t stream) {
 // one block barrier per chunk orders them.  EPI_PARTIAL splits the contraction into
 // bt.ksplit slices and writes each slice's fp32 sums to part_val[slice][m][n] for the
 // finalize pass.  The LDS layout is tile_lds()'s.
-#ifndef MEDUSA_TILE_SWIZZLE
-#define MEDUSA_TILE_SWIZZLE 1
-#endif
 template <int WM, int WN, int MTW, int RTW, bool DB = false>
 constexpr size_t tile_lds() {
     return (size_t)(16 * WM * MTW + 16 * WN * RTW) * (MEDUSA_TILE_SWIZZLE ? 64 : 64 + 8) * 2 * (DB ? 2 : 1) +
@@ -1705,13 +1724,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
     constexpr int TM = 16 * WM * MTW;           // input rows per tile
     constexpr int TN = 16 * WN * RTW;           // weight rows per tile
     constexpr int CH = 64;
-    // LDS rows of CH elements (128 B, 8 units of 16 B) with no padding: unit u of row r is
-    // stored at unit u ^ ((r >> 1) & 7).  A 16-lane group's 16-byte stores then cover two
-    // whole rows (64 distinct banks) and its fragment reads (16 rows, one unit each) hit
-    // 16 distinct 4-bank groups; a padded pitch of 72 made every store pair overlap.
-    constexpr int XP = MEDUSA_TILE_SWIZZLE ? CH : CH + 8;
+    constexpr int XP = MEDUSA_TILE_SWIZZLE ? CH : CH + 8;    // see sw64()
     auto sw = [](int row, int col) __attribute__((always_inline)) {   // element offset in an LDS tile
-        return MEDUSA_TILE_SWIZZLE ? row * CH + ((((col >> 3) ^ (row >> 1)) & 7) << 3) : row * (CH + 8) + col;
+        return MEDUSA_TILE_SWIZZLE ? sw64(row, col) : row * (CH + 8) + col;
     };
     constexpr int LPR = CH / 8;                 // lanes per row per load instruction
     constexpr int RPI = NT / LPR;               // rows per workgroup load instruction
@@ -2090,7 +2105,8 @@ bool gemv_eligible(medusa_dtype dt, int epi, const GemmBatch& bt) {
 // tiles, the per-wave epilogue reductions.
 template <int MT, int RTW, int CH, int NWV>
 constexpr size_t rowstream_lds() {
-    return (size_t)(MT * 16 * (CH + 8) + 8) * 2 + (size_t)NWV * 16 * RTW * (CH + 8) * 2 +
+    constexpr int XP = MEDUSA_RS_SWIZZLE && CH == 64 ? CH : CH + 8;
+    return (size_t)(MT * 16 * XP + 8) * 2 + (size_t)NWV * 16 * RTW * XP * 2 +
            (size_t)NWV * MT * 16 * 8;
 }
 
@@ -2145,10 +2161,12 @@ hipError_t launch_rowstream_m(GemmBatch& bt, hipStream_t stream) {
 // Up to 64 rows over a small vocabulary: 4-wave workgroups (128-row tiles).
 template <int EPI>
 hipError_t launch_rowstream_small(GemmBatch& bt, hipStream_t stream) {
-    constexpr int W = kRsWavesSmallVocab, RT = kRsRtwSmallVocab;
-    if (bt.M <= 16) return launch_rowstream_t<1, EPI, RT, kRsPf, kRsChunk, W>(bt, stream);
-    if (bt.M <= 32) return launch_rowstream_t<2, EPI, RT, kRsPf, kRsChunk, W>(bt, stream);
-    return launch_rowstream_t<4, EPI, RT, kRsPf, kRsChunk, W>(bt, stream);
+    constexpr int W = kRsWavesSmallVocab, RT = kRsRtwSmallVocab, PF = MEDUSA_RS_PF_SMALLV;
+    constexpr int CH = MEDUSA_RS_CHUNK_SMALLV;
+    if (bt.K % CH != 0) return hipErrorInvalidValue;
+    if (bt.M <= 16) return launch_rowstream_t<1, EPI, RT, PF, CH, W>(bt, stream);
+    if (bt.M <= 32) return launch_rowstream_t<2, EPI, RT, PF, CH, W>(bt, stream);
+    return launch_rowstream_t<4, EPI, RT, PF, CH, W>(bt, stream);
 }
 
 hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
