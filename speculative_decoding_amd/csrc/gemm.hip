@@ -218,6 +218,23 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_store_kernel(const GemmB
     store_epilogue<T, MT, RT>(P, bt, acc, m0, n_wave, ln, lg);
 }
 
+#ifndef MEDUSA_SR_SWIZZLE
+#define MEDUSA_SR_SWIZZLE 1
+#endif
+#ifndef MEDUSA_RS_SWIZZLE
+#define MEDUSA_RS_SWIZZLE 1
+#endif
+#ifndef MEDUSA_TILE_SWIZZLE
+#define MEDUSA_TILE_SWIZZLE 1
+#endif
+// LDS tiles of 64-element rows (128 B, 8 units of 16 B) with no padding: unit u of row r is
+// stored at unit u ^ ((r >> 1) & 7).  A 16-lane group's 16-byte stores (two whole rows)
+// then cover 64 distinct banks and its MFMA fragment reads (16 rows, one unit each) hit 16
+// distinct 4-bank groups; a padded pitch of 72 made every pair of stored rows overlap.
+__device__ __forceinline__ int sw64(int row, int col) {
+    return row * 64 + ((((col >> 3) ^ (row >> 1)) & 7) << 3) + (col & 7);
+}
+
 // The same split for bf16 when every quarter of the contraction is whole 64-wide chunks:
 // each wave streams its RT*16 weight rows over its quarter with row-contiguous loads (8
 // rows x 128 B per instruction, the pattern that streams HBM fastest) into a wave-private,
@@ -230,7 +247,9 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_rows_kernel(const GemmBa
     constexpr int CH = kSplitRowsChunk;
     constexpr int KW = kWaves;
     constexpr int ROWS = 16 * RT;
-    constexpr int XP = CH + 8;                // LDS pitch of a weight row (elements)
+    constexpr bool SWZ = MEDUSA_SR_SWIZZLE && CH == 64;
+    constexpr int XP = SWZ ? CH : CH + 8;     // LDS pitch of a weight row (elements)
+    auto at = [](int row, int c) __attribute__((always_inline)) { return SWZ ? sw64(row, c) : row * XP + c; };
     constexpr int LPR = CH / 8;               // lanes per weight row per load instruction
     constexpr int RPI = kWave / LPR;          // weight rows per load instruction
     constexpr int NI = ROWS / RPI;            // weight loads per lane per chunk
@@ -309,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_rows_kernel(const GemmBa
     auto store_w = [&](int p, int buf) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            *reinterpret_cast<u32x4*>(&wt[buf * ROWS * XP + (RPI * i + half) * XP + col]) = wr[p][i];
+            *reinterpret_cast<u32x4*>(&wt[buf * ROWS * XP + at(RPI * i + half, col)]) = wr[p][i];
     };
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
@@ -336,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_rows_kernel(const GemmBa
         for (int ks = 0; ks < KS; ++ks) {
             Frag<bf16_t> wf[RT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) wf[rt].load(wb + (rt * 16 + ln) * XP + 32 * ks + 8 * lg);
+            for (int rt = 0; rt < RT; ++rt) wf[rt].load(wb + at(rt * 16 + ln, 32 * ks + 8 * lg));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -776,20 +795,6 @@ constexpr int kRsRtwArgmax = MEDUSA_RS_RTW_ARGMAX;
 constexpr int kRsWavesSmallVocab = MEDUSA_RS_WAVES_SMALLV;
 constexpr int kRsRtwSmallVocab = MEDUSA_RS_RTW_SMALLV;
 bool rs_small_vocab(int M, int N) { return M <= 64 && N < MEDUSA_RS_SMALL_VOCAB; }
-
-#ifndef MEDUSA_RS_SWIZZLE
-#define MEDUSA_RS_SWIZZLE 1
-#endif
-#ifndef MEDUSA_TILE_SWIZZLE
-#define MEDUSA_TILE_SWIZZLE 1
-#endif
-// LDS tiles of 64-element rows (128 B, 8 units of 16 B) with no padding: unit u of row r is
-// stored at unit u ^ ((r >> 1) & 7).  A 16-lane group's 16-byte stores (two whole rows)
-// then cover 64 distinct banks and its MFMA fragment reads (16 rows, one unit each) hit 16
-// distinct 4-bank groups; a padded pitch of 72 made every pair of stored rows overlap.
-__device__ __forceinline__ int sw64(int row, int col) {
-    return row * 64 + ((((col >> 3) ^ (row >> 1)) & 7) << 3) + (col & 7);
-}
 
 template <int MT, int EPI, int RTW, int PF, int CH, int NWV>
 __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmBatch bt) {
