@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, MI355X (vendor)
 DOMINANT = "heads_vocab"        # the kernel with most of the step's bytes (A2+A3)
 # HBM bytes of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, valid while
 # the sources it was measured on are unchanged (their hash is recorded beside the figure)
@@ -336,6 +337,69 @@ def cpu_baseline(inp, oplan, reps: int = 3) -> dict:
             "seconds_per_step": dt, "accept_len": [int(a) for a in res.accept_len]}
 
 
+def attention_only(args) -> int:
+    """medusa_tree_attention alone at one workload's shapes: its plan, heads, head dim,
+    prefix lengths and cache capacity, on seeded random bf16 inputs.  Both launches are
+    event-timed by the library's profiler over `--attention-calls` calls after five
+    warm-up calls."""
+    import torch
+
+    from speculative_decoding_amd import medusa as M
+    from synth import get_config
+    from synth.gen import _prefix_lens, accuracy_table
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        return 1
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    plan = (M.medusa_tree_plan_full(cfg.tree_s) if cfg.tree == "full" else
+            M.medusa_tree_plan_from_accuracy(accuracy_table(cfg, args.seed), cfg.tree_s, cfg.n_nodes))
+    plan.upload(dev)
+    B, N, Hq, Hkv, d, Lcap = cfg.B, plan.n_nodes, cfg.Hq, cfg.Hkv, cfg.d, cfg.Lcap
+    lens = [int(x) for x in _prefix_lens(cfg, args.seed)]
+    g = torch.Generator(device=dev).manual_seed(args.seed)
+    mk = lambda *shape: torch.randn(*shape, device=dev, generator=g).to(torch.bfloat16)
+    q, kt, vt = mk(B, N, Hq, d), mk(B, N, Hkv, d), mk(B, N, Hkv, d)
+    kc, vc = mk(B, Lcap, Hkv, d), mk(B, Lcap, Hkv, d)
+    L = torch.as_tensor(lens, device=dev, dtype=torch.int32)
+    out = torch.empty(B, N, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(M.medusa_attention_workspace(plan, "bf16", B, Hq, Hkv, d, Lcap),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        M.medusa_tree_attention(plan, "bf16", B, Hq, Hkv, d, Lcap, 0.0, q, kt, vt, kc, vc, L, out, ws)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    M.medusa_profile_reset()
+    M.medusa_profile_enable(True)
+    for _ in range(args.attention_calls):
+        call()
+    torch.cuda.synchronize()
+    M.medusa_profile_enable(False)
+    tile_ms, tile_n = M.medusa_profile_query("attn_partial")
+    merge_ms, merge_n = M.medusa_profile_query("attn_combine")
+    tile_us, merge_us = 1e3 * tile_ms / tile_n, 1e3 * merge_ms / merge_n
+    keys = sum(min(x, Lcap) for x in lens) + B * N
+    flop = 4.0 * N * Hq * d * keys                     # scores and value sums, every (row, key)
+    kv_bytes = 2 * 2 * d * Hkv * sum(min(x, Lcap) for x in lens)
+    print(json.dumps({
+        "metric": "tree attention alone (medusa_tree_attention)", "config": args.config,
+        "library": os.path.relpath(_lib_path(), ROOT), "B": B, "nodes": N, "Hq": Hq, "Hkv": Hkv, "d": d,
+        "prefix": lens, "calls": args.attention_calls, "tile_us": tile_us, "merge_us": merge_us,
+        "gflop": flop / 1e9, "tflops": flop / (tile_us + merge_us) / 1e6,
+        "mfma_frac": flop / (tile_us + merge_us) / 1e6 / MFMA_PEAK_TFLOPS,
+        "kv_bytes": kv_bytes, "workspace_bytes": ws.numel()}))
+    return 0
+
+
+def _lib_path() -> str:
+    from speculative_decoding_amd import _lib
+    return _lib.LIB_PATH
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,7 +421,19 @@ def main() -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run an elementwise kernel that reads and writes this many MiB once before "
                          "the timed region (known sizes to calibrate rocprofv3 byte counters)")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="time medusa_tree_attention alone at this workload's shapes on seeded "
+                         "random bf16 inputs and print one JSON line of its own (not the step metric)")
+    ap.add_argument("--attention-calls", type=int, default=50)
+    ap.add_argument("--lib", default=None,
+                    help="load this libmedusa.so instead of the in-tree build (a build of an "
+                         "earlier revision, for before / after counters; with --attention-only)")
     args = ap.parse_args()
+    if args.lib:
+        from speculative_decoding_amd import _lib
+        _lib.use_library(args.lib)
+    if args.attention_only:
+        return attention_only(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)

@@ -89,6 +89,20 @@ def header_functions():
     return sorted(set(re.findall(r"\b(medusa_[a-z0-9_]+)\s*\(", text)))
 
 
+_LENIENT = False
+
+
+def use_library(path: str) -> None:
+    """Load `path` instead of the in-tree build, e.g. a build of an earlier revision for a
+    before / after measurement; entry points that build lacks are left unbound.  Must be
+    called before the first lib()."""
+    global LIB_PATH, _LENIENT
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = os.path.abspath(path)
+    _LENIENT = True
+
+
 def lib() -> ctypes.CDLL:
     """Load libmedusa.so; raises if it has not been built (there is no fallback)."""
     global _lib
@@ -98,6 +112,8 @@ def lib() -> ctypes.CDLL:
                                "(python -m speculative_decoding_amd.build)")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
+            if _LENIENT and not hasattr(L, name):
+                continue
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
