@@ -84,8 +84,13 @@ struct AttnArgs {
     const void* v_cache;
     const int32_t* prefix_lens;
     void* out;
-    float* ws_o;    // fp32 kernel: [B][Hkv][slots][rows][d]; bf16: [workgroup][rows][d]
-    float* ws_ml;   // the same rows x (running maximum, sum)
+    float* ws_o;    // fp32 kernel: [B][Hkv][slots][rows][d] unnormalised partial outputs;
+                    // bf16 kernel: [workgroup][rows][d] normalised partials in fp32, written
+                    // only by the fp32 recomputation
+    float* ws_ml;   // fp32 kernel: the same rows x (running maximum, sum);
+                    // bf16 kernel: [workgroup][rows] x (maximum, sum, 1 if the row is in
+                    // ws_o else 0, unused)
+    uint16_t* ws_h; // bf16 kernel: [workgroup][rows][d] normalised partial outputs as fp16
     int* ws_plan;   // bf16: [B] first workgroup slot of each sequence, then [B] slot counts
 };
 
@@ -451,6 +456,12 @@ __global__ __launch_bounds__(NWV * 64) void attn_partial_kernel(const AttnArgs a
 
 // ------------------------------------------------------------------ bf16: 32 x 32 tiles
 
+// Element e (0..7) of eight bf16 values held as four words, as fp32 (exact).
+__device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
+    const uint32_t w = v[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -470,12 +481,13 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     const f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
     return __builtin_bit_cast(uint32_t, v);
 }
-// Element e (0..7) of eight bf16 values held as four words, as fp32 (exact).
-__device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
+// Element e (0..7) of eight fp16 values held as four words, as fp32 (exact).
+__device__ __forceinline__ float f16_elem(const u32x4& v, int e) {
+    // through a scalar: a bit cast applied to the vector subscript itself reads word 0
     const uint32_t w = v[e >> 1];
-    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    const f16x2 p = __builtin_bit_cast(f16x2, w);
+    return static_cast<float>(p[e & 1]);
 }
-
 // The rows [row0, row0 + nrows) of one (sequence, kv head) over one key range, in fp32 on
 // the vector units straight from global memory, one row per thread: scores, their maximum
 // and sum, then the unnormalised output 32 head-dim elements at a time.  Written for
@@ -516,6 +528,9 @@ __device__ __noinline__ void attn_rows_fp32(const bf16_t* q, const bf16_t* kpre,
     float l = 0.f;
     for (int j = 0; j < n_all; ++j)
         if (visible(j)) l += exp2f(score(j) - mb);
+    // stored normalised and in fp32: values beyond fp16's range, whose contributions the
+    // merge may cancel, keep their full precision
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     float* wo = wo_base + (long long)r * D;
     for (int c = 0; c < D; c += 32) {
         float acc[32];
@@ -526,10 +541,11 @@ __device__ __noinline__ void attn_rows_fp32(const bf16_t* q, const bf16_t* kpre,
             const bf16_t* vr = row_v(j) + c;
             for (int e = 0; e < 32; ++e) acc[e] += p * bf16_to_f32(vr[e]);
         }
-        for (int e = 0; e < 32; ++e) wo[c + e] = acc[e];
+        for (int e = 0; e < 32; ++e) wo[c + e] = acc[e] * inv;
     }
-    ml_base[2 * r + 0] = m;
-    ml_base[2 * r + 1] = l;
+    ml_base[4 * r + 0] = m;
+    ml_base[4 * r + 1] = l;
+    ml_base[4 * r + 2] = 1.f;
 }
 
 // Compile-time tuning overrides (0: chosen from the shape).
@@ -849,7 +865,7 @@ void attn_tile_kernel(const AttnArgs a) {
     if (fallback)
         attn_rows_fp32<D>(static_cast<const bf16_t*>(a.q) + (long long)b * sh.N * sh.Hq * D, kpre,
                           vpre, ktr, vtr, a.plan.mask, a.plan.mask_words, a.ws_o + slot_base * D,
-                          a.ws_ml + slot_base * 2, sh.rows, sh.N, sh.G, sh.Hq, g, kstride,
+                          a.ws_ml + slot_base * 4, sh.rows, sh.N, sh.G, sh.Hq, g, kstride,
                           a.scale_log2, qb * ROWS, ROWS, p_begin, p_end, with_tree);
 
     // The only slot of its sequence writes the attention output straight from its
@@ -881,37 +897,37 @@ void attn_tile_kernel(const AttnArgs a) {
             if (r >= sh.rows) continue;
             const int part = i % (D / 8);
             const long long bs = slot_base + r;
-            const float inv = 1.f / a.ws_ml[bs * 2 + 1];
-            const floatx4* src = reinterpret_cast<const floatx4*>(a.ws_o + bs * D + part * 8);
-            const floatx4 v0 = src[0], v1 = src[1];
+            const floatx4 f0 = *reinterpret_cast<const floatx4*>(a.ws_o + bs * D + part * 8);
+            const floatx4 f1 = *reinterpret_cast<const floatx4*>(a.ws_o + bs * D + part * 8 + 4);
+            const float v[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
             bf16_t* orow = out + (((long long)b * sh.N + r / sh.G) * sh.Hq + g * sh.G + r % sh.G) * D + part * 8;
-            *reinterpret_cast<u32x4*>(orow) =
-                u32x4{pack_bf16x2(v0[0] * inv, v0[1] * inv), pack_bf16x2(v0[2] * inv, v0[3] * inv),
-                      pack_bf16x2(v1[0] * inv, v1[1] * inv), pack_bf16x2(v1[2] * inv, v1[3] * inv)};
+            *reinterpret_cast<u32x4*>(orow) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
         }
         return;
     }
 
-    // Otherwise the partial (unnormalised output, running maximum, sum) goes to the
-    // workspace for attn_merge_kernel.
+    // Otherwise the partial goes to the workspace for attn_merge_kernel: the normalised
+    // output o / l as fp16 (a convex combination of values that all fit fp16 on this
+    // path), and the running maximum and sum.
     if (!fallback) {
 #pragma unroll
         for (int t = 0; t < R; ++t) {
             const float l_row = sum_xor32(l_sum[t]);
             if (!row_ok[t]) continue;
+            const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
             const int r = qb * ROWS + (wave * R + t) * 32 + l32;
             const long long base = slot_base + r;
-            float* wo = a.ws_o + base * D;
+            uint16_t* wo = a.ws_h + base * D;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<floatx4*>(wo + 32 * dt + 8 * j + 4 * hi) =
-                        floatx4{o[t][dt][4 * j], o[t][dt][4 * j + 1], o[t][dt][4 * j + 2], o[t][dt][4 * j + 3]};
-            if (hi == 0) {
-                a.ws_ml[base * 2 + 0] = m_used[t];
-                a.ws_ml[base * 2 + 1] = l_row;
-            }
+                    *reinterpret_cast<uint2*>(wo + 32 * dt + 8 * j + 4 * hi) =
+                        uint2{pack_f16x2(o[t][dt][4 * j] * inv, o[t][dt][4 * j + 1] * inv),
+                              pack_f16x2(o[t][dt][4 * j + 2] * inv, o[t][dt][4 * j + 3] * inv)};
+            if (hi == 0)
+                *reinterpret_cast<floatx4*>(a.ws_ml + base * 4) = floatx4{m_used[t], l_row, 0.f, 0.f};
         }
     }
 }
@@ -945,30 +961,36 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
     float mx = -INFINITY, den = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < n; s0 += MAXJ) {
-        float ms[MAXJ], ls[MAXJ];
-        floatx4 v0[MAXJ], v1[MAXJ];
+        floatx4 ml[MAXJ];
+        u32x4 hv[MAXJ];
 #pragma unroll
         for (int u = 0; u < MAXJ; ++u) {
             const int sl = min(s0 + u, n - 1);
             const long long bs = base0 + (long long)sl * step;
-            ms[u] = a.ws_ml[bs * 2];
-            ls[u] = a.ws_ml[bs * 2 + 1];
-            const floatx4* src = reinterpret_cast<const floatx4*>(a.ws_o + bs * D + part * 8);
-            v0[u] = src[0];
-            v1[u] = src[1];
+            ml[u] = *reinterpret_cast<const floatx4*>(a.ws_ml + bs * 4);
+            hv[u] = *reinterpret_cast<const u32x4*>(a.ws_h + bs * D + part * 8);
         }
 #pragma unroll
         for (int u = 0; u < MAXJ; ++u) {
-            if (s0 + u >= n || ms[u] == -INFINITY) continue;
-            const float m_new = fmaxf(mx, ms[u]);
-            const float alpha = mx == -INFINITY ? 0.f : exp2f(mx - m_new);
-            const float w = exp2f(ms[u] - m_new);
-            den = den * alpha + w * ls[u];
+            if (s0 + u >= n || ml[u][0] == -INFINITY) continue;
+            // slot u holds o_u / l_u (fp16, or fp32 after the recomputation) and its
+            // maximum m_u and sum l_u
+            float v[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[e] = acc[e] * alpha + w * v0[u][e];
-                acc[4 + e] = acc[4 + e] * alpha + w * v1[u][e];
+            for (int e = 0; e < 8; ++e) v[e] = f16_elem(hv[u], e);
+            if (ml[u][2] != 0.f) {
+                const float* f = a.ws_o + (base0 + (long long)(s0 + u) * step) * D + part * 8;
+                const floatx4 f0 = *reinterpret_cast<const floatx4*>(f);
+                const floatx4 f1 = *reinterpret_cast<const floatx4*>(f + 4);
+                v[0] = f0[0]; v[1] = f0[1]; v[2] = f0[2]; v[3] = f0[3];
+                v[4] = f1[0]; v[5] = f1[1]; v[6] = f1[2]; v[7] = f1[3];
             }
+            const float m_new = fmaxf(mx, ml[u][0]);
+            const float alpha = mx == -INFINITY ? 0.f : exp2f(mx - m_new);
+            const float w = exp2f(ml[u][0] - m_new) * ml[u][1];
+            den = den * alpha + w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = acc[e] * alpha + w * v[e];
             mx = m_new;
         }
     }
@@ -1154,8 +1176,17 @@ static size_t attn_partial_rows(const AttnShape& s) {
     return (size_t)s.B * s.Hkv * s.n_slots * s.rows;
 }
 
+// bf16: byte offset of the fp32 rows that the recomputation writes (256-byte aligned)
+static size_t attn_f32_rows_offset(const AttnShape& s) {
+    const size_t rows = attn_partial_rows(s);
+    const size_t head = rows * (size_t)s.d * 2 + rows * 4 * sizeof(float) + (size_t)s.B * 2 * sizeof(int);
+    return (head + 255) / 256 * 256;
+}
+
 size_t attn_workspace_bytes(const AttnShape& s) {
     const size_t rows = attn_partial_rows(s);
+    if (s.tile_r > 0)      // fp16 rows, (maximum, sum, flag, -) per row, the plan, fp32 rows
+        return attn_f32_rows_offset(s) + rows * (size_t)s.d * sizeof(float);
     return rows * (size_t)s.d * sizeof(float) + rows * 2 * sizeof(float) + (size_t)s.B * 2 * sizeof(int) + 256;
 }
 
@@ -1171,9 +1202,17 @@ hipError_t attention_launch(medusa_dtype dt, const AttnShape& s, const DevicePla
     a.prefix_lens = prefix_lens;
     a.out = out;
     const size_t rows = attn_partial_rows(s);
-    a.ws_o = static_cast<float*>(ws);
-    a.ws_ml = a.ws_o + rows * s.d;
-    a.ws_plan = reinterpret_cast<int*>(a.ws_ml + rows * 2);
+    if (s.tile_r > 0) {
+        a.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_f32_rows_offset(s));
+        a.ws_h = static_cast<uint16_t*>(ws);
+        a.ws_ml = reinterpret_cast<float*>(a.ws_h + rows * s.d);     // 16-byte aligned: d % 64 == 0
+        a.ws_plan = reinterpret_cast<int*>(a.ws_ml + rows * 4);
+    } else {
+        a.ws_h = nullptr;
+        a.ws_o = static_cast<float*>(ws);
+        a.ws_ml = a.ws_o + rows * s.d;
+        a.ws_plan = reinterpret_cast<int*>(a.ws_ml + rows * 2);
+    }
     if (dt == MEDUSA_BF16) {
         return s.d == 64 ? launch_td<bf16_t, 64>(a, stream) : launch_td<bf16_t, 128>(a, stream);
     }
