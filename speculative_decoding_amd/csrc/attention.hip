@@ -490,9 +490,10 @@ __device__ __forceinline__ float f16_elem(const u32x4& v, int e) {
 }
 // The rows [row0, row0 + nrows) of one (sequence, kv head) over one key range, in fp32 on
 // the vector units straight from global memory, one row per thread: scores, their maximum
-// and sum, then the unnormalised output 32 head-dim elements at a time.  Written for
-// correctness only: it serves the rare key range whose fp16 value path overflowed.  Kept
-// out of line so that it adds no registers to the tiled kernel.
+// and sum, then the output divided by the sum, 32 head-dim elements at a time, into the
+// fp32 rows at wo_base (and (maximum, sum, 1) into ml_base).  Written for correctness
+// only: it serves the rare key range whose fp16 value path overflowed.  Kept out of line
+// so that it adds no registers to the tiled kernel.
 template <int D>
 __device__ __noinline__ void attn_rows_fp32(const bf16_t* q, const bf16_t* kpre, const bf16_t* vpre,
                                             const bf16_t* ktr, const bf16_t* vtr,
