@@ -482,6 +482,12 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 // Element e (0..7) of eight fp16 values held as four words, as fp32 (exact).
+// acc + the two fp16 halves of w, in fp32 (one v_dot2_f32_f16 against (1, 1)): the row
+// sums then add exactly the fp16 probabilities that the value MFMAs multiply.
+__device__ __forceinline__ float sum_f16x2(uint32_t w, float acc) {
+    const f16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+}
 __device__ __forceinline__ float f16_elem(const u32x4& v, int e) {
     // through a scalar: a bit cast applied to the vector subscript itself reads word 0
     const uint32_t w = v[e >> 1];
@@ -783,8 +789,9 @@ void attn_tile_kernel(const AttnArgs a) {
                     for (int w = 0; w < 4; ++w) {
                         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * kk + 2 * w], c2, -mb));
                         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * kk + 2 * w + 1], c2, -mb));
-                        pf[t][kk][w] = pack_f16x2(p0, p1);
-                        ls += p0 + p1;
+                        const uint32_t pw = pack_f16x2(p0, p1);
+                        pf[t][kk][w] = pw;
+                        ls = sum_f16x2(pw, ls);
                     }
                 l_sum[t] += ls;
             }
