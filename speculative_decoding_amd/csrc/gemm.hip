@@ -759,6 +759,15 @@ constexpr int kRsChunk = MEDUSA_RS_CHUNK;   // contraction chunk per pass
 constexpr int kRsRtw = MEDUSA_RS_RTW;       // 16-row weight tiles per wave (top-s)
 constexpr int kRsWavesTops = MEDUSA_RS_WAVES_TOPS;
 constexpr int kRsPf = MEDUSA_RS_PF;         // chunks in flight ahead of the one multiplied
+// The top-s path (heads from batch 3) streams 256-wide chunks: at batch 8 of the 70B shape
+// heads_vocab took 391.7 us against 413.8 with 64-wide chunks (128: 412.0; 512: 420.3),
+// 0.96 of the read probe.  Each chunk costs two block barriers and an LDS round trip, which
+// a wider chunk pays less often per weight byte.  Contractions that 256 does not divide
+// keep the 64-wide chunk.
+#ifndef MEDUSA_RS_CHUNK_TOPS
+#define MEDUSA_RS_CHUNK_TOPS 256
+#endif
+constexpr int kRsChunkTops = MEDUSA_RS_CHUNK_TOPS;
 constexpr int kPartialChunk = 64;           // contraction chunk of the slice kernels
 constexpr int kWavePartialRows = 64;        // weight rows per single-wave slice tile
 #ifndef MEDUSA_RS_WAVES_ARGMAX
@@ -2186,7 +2195,9 @@ hipError_t launch_rowstream_small(GemmBatch& bt, hipStream_t stream) {
 
 hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
     if (epi == EPI_TOPS)
-        return launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunk, kRsWavesTops>(bt, stream);
+        return bt.K % kRsChunkTops == 0
+                   ? launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunkTops, kRsWavesTops>(bt, stream)
+                   : launch_rowstream_t<1, EPI_TOPS, kRsRtw, kRsPf, kRsChunk, kRsWavesTops>(bt, stream);
     // the tile size follows each problem's width (gemm_rows_per_tile): one launch needs
     // them all on the same side
     int small = 0;
@@ -2200,7 +2211,7 @@ hipError_t launch_rowstream(int epi, GemmBatch& bt, hipStream_t stream) {
     return launch_rowstream_m<EPI_ARGMAX, kRsRtwArgmax, kRsPf, kRsChunk, kRsWavesArgmax>(bt, stream);
 }
 
-// Row-streaming MFMA path: bf16, contraction a multiple of its 256-wide chunk, argmax or
+// Row-streaming MFMA path: bf16, contraction a multiple of 64, argmax or
 // top-s epilogue (top-s only past the GEMV's two rows).
 bool rowstream_eligible(medusa_dtype dt, int epi, int M, int K) {
     if (dt != MEDUSA_BF16 || K % kRsChunk != 0) return false;

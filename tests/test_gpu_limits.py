@@ -82,23 +82,25 @@ def test_vocabulary_tile_boundary(dev, V):
     compare_step(inp, got, ref, plan=plan)
 
 
-def test_contraction_off_256(dev):
-    """Verification over a small vocabulary streams 256-wide contraction chunks when 256
-    divides the hidden size and 64-wide chunks otherwise: a whole step of the small shape
-    with H = 448 (a multiple of 64, not of 256), unplanted, so accept results follow the
-    device's decisions."""
+@pytest.mark.parametrize("base", ["small", "small_batched"])
+def test_contraction_off_256(dev, base):
+    """Verification over a small vocabulary, and the heads from batch 3, stream 256-wide
+    contraction chunks when 256 divides the hidden size and 64-wide chunks otherwise: a
+    whole step with H = 448 (a multiple of 64, not of 256) at one sequence and at three,
+    unplanted, so accept results follow the device's decisions."""
     import dataclasses
     from synth import get_config
-    say("[limits: hidden 448]")
-    cfg = dataclasses.replace(get_config("small"), name="small_h448", H=448)
+    say(f"[limits: {base}, hidden 448]")
+    cfg = dataclasses.replace(get_config(base), name=f"{base}_h448", H=448)
     inp = make_inputs(cfg, 0)
     plan = oracle_plan(inp)
     ref = oracle.step(inp, plan)
-    r = np.sort(ref.root_logits[0])[-2:]
-    assert r[1] - r[0] >= 1e-4, "the draw has a near-tie at the root"
-    for k in range(cfg.K):
-        v = np.sort(ref.head_logits[0, k])[::-1][: cfg.s[k] + 1]
-        assert np.min(v[:-1] - v[1:]) >= 1e-4, "the draw has a near-tie in a head's top-k"
+    for b in range(cfg.B):
+        r = np.sort(ref.root_logits[b])[-2:]
+        assert r[1] - r[0] >= 1e-4, "the draw has a near-tie at a root"
+        for k in range(cfg.K):
+            v = np.sort(ref.head_logits[b, k])[::-1][: cfg.s[k] + 1]
+            assert np.min(v[:-1] - v[1:]) >= 1e-4, "the draw has a near-tie in a head's top-k"
     _, got = run_gpu(inp, dev, keep_logits=True)
     compare_step(inp, got, ref, plan=plan)
     say(f"    accept {got['accept_len'].tolist()}")
