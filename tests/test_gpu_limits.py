@@ -104,3 +104,27 @@ def test_contraction_off_256(dev, base):
     _, got = run_gpu(inp, dev, keep_logits=True)
     compare_step(inp, got, ref, plan=plan)
     say(f"    accept {got['accept_len'].tolist()}")
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_small_vocabulary_row_blocks(dev, B):
+    """Verification over a small vocabulary takes 16-, 32- or 64-row input blocks: the
+    small batched shape (16-node trees) at one and two sequences verifies 16 and 32 rows,
+    unplanted, so accept results follow the device's decisions."""
+    import dataclasses
+    from synth import get_config
+    say(f"[limits: small_batched, B={B}]")
+    base = get_config("small_batched")
+    cfg = dataclasses.replace(base, name=f"small_batched_b{B}", B=B, lens=base.lens[:B])
+    inp = make_inputs(cfg, 0)
+    plan = oracle_plan(inp)
+    ref = oracle.step(inp, plan)
+    for b in range(cfg.B):
+        r = np.sort(ref.root_logits[b])[-2:]
+        assert r[1] - r[0] >= 1e-4, "the draw has a near-tie at a root"
+        for k in range(cfg.K):
+            v = np.sort(ref.head_logits[b, k])[::-1][: cfg.s[k] + 1]
+            assert np.min(v[:-1] - v[1:]) >= 1e-4, "the draw has a near-tie in a head's top-k"
+    _, got = run_gpu(inp, dev, keep_logits=True)
+    compare_step(inp, got, ref, plan=plan)
+    say(f"    accept {got['accept_len'].tolist()}")
