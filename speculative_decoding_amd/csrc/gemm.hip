@@ -1845,12 +1845,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
             Frag<bf16_t> wf[RTW];
 #pragma unroll
             for (int rt = 0; rt < RTW; ++rt) wf[rt].load(ws + sw(wn + rt * 16 + ln, ks + 8 * lg));
+            // the next X fragment is read while the current one's MFMAs run
+            Frag<bf16_t> xf[2];
+            xf[0].load(xs + sw(wm + ln, ks + 8 * lg));
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) {
-                Frag<bf16_t> xf;
-                xf.load(xs + sw(wm + mt * 16 + ln, ks + 8 * lg));
+                if (mt + 1 < MTW) xf[(mt + 1) & 1].load(xs + sw(wm + (mt + 1) * 16 + ln, ks + 8 * lg));
 #pragma unroll
-                for (int rt = 0; rt < RTW; ++rt) mma(acc[rt][mt], xf, wf[rt]);
+                for (int rt = 0; rt < RTW; ++rt) mma(acc[rt][mt], xf[mt & 1], wf[rt]);
             }
         }
     };
