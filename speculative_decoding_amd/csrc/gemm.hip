@@ -1840,6 +1840,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
     auto multiply = [&](const bf16_t* st) {     // acc += the chunk in one LDS stage
         const bf16_t* xs = st;
         const bf16_t* ws = st + TM * XP;
+        // a wave raises its issue priority while it multiplies, so that the waves sharing
+        // its SIMD and still staging a chunk yield the issue slots to the matrix work
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < CH; ks += 32) {
             Frag<bf16_t> wf[RTW];
@@ -1855,6 +1858,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
                 for (int rt = 0; rt < RTW; ++rt) mma(acc[rt][mt], xf[mt & 1], wf[rt]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     if (n_ch > 0) load(0);
