@@ -898,10 +898,17 @@ __global__ __launch_bounds__(NWV * kWave) void gemm_rowstream_kernel(const GemmB
     // load is issued on every path (refills past the slice re-read its last chunk) so the
     // compiler's wait counts stay exact: storing slot p waits only for slot p's loads.
     const int n_ch = (k_hi - k_lo) / CH;
+    // With 64-wide chunks every tile starts its walk over the contraction at its own
+    // chunk (the sums are taken in that rotated order).  Tiles that all read the same
+    // column offset of their 8 KiB-strided rows at the same moment otherwise crowd the
+    // same memory channels: 8B-shape verification 168.6 -> 160.5 us.
+    const int rot = CH == 64 && n_ch > 0 ? (int)(((unsigned)tile * 37u) % (unsigned)n_ch) : 0;
     u32x4 wr[PF][NI];
     u32x4 xr[PF][XV];
     auto load = [&](int p, int c) {
-        const int kc = k_lo + min(c, n_ch - 1) * CH;
+        int cr = min(c, n_ch - 1) + rot;
+        if (cr >= n_ch) cr -= n_ch;
+        const int kc = k_lo + cr * CH;
 #pragma unroll
         for (int i = 0; i < NI; ++i) wr[p][i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
 #pragma unroll
@@ -1813,8 +1820,17 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_tile_kernel(const GemmBa
     const int c_lo = min(chunks, ksl * per);
     const int n_ch = min(chunks, (ksl + 1) * per) - c_lo;
     u32x4 xr[XL], wr[WL];
+    // Verification tiles start their walk over the contraction at a chunk of their own
+    // (both row blocks of a W tile at the same one, so the tile still leaves HBM once),
+    // which spreads the reads of concurrent tiles over the memory channels, when all of X
+    // fits an XCD's L2 comfortably (at most 2 MiB): dense tree 223.8 -> 214.4 us.  With a
+    // larger X (batched 70B, 8 MiB) the rotated walks no longer share X in L2 and lose.
+    const int rot = EPI == EPI_ARGMAX && n_ch > 0 && (long long)bt.M * K * 2 <= (2ll << 20)
+                        ? (int)(((unsigned)t * 37u) % (unsigned)n_ch) : 0;
     auto load = [&](int c) {
-        const int kc = (c_lo + min(c, n_ch - 1)) * CH;
+        int cr = min(c, n_ch - 1) + rot;
+        if (cr >= n_ch) cr -= n_ch;
+        const int kc = (c_lo + cr) * CH;
 #pragma unroll
         for (int i = 0; i < XL; ++i) xr[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kc);
 #pragma unroll
