@@ -309,13 +309,18 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_rows_kernel(const GemmBa
     // quarter re-read its last one) so the compiler's wait counts stay exact
     u32x4 wr[PF][NI];
     Frag<bf16_t> xr[PF][MT][KS];
+    // each tile walks its quarter from a chunk of its own (sums in that rotated order), so
+    // concurrent tiles do not all read the same column offset of their 16 KiB-strided
+    // rows at once: batched 70B heads 112.7 -> 109.7 us
+    const int rot = n_ch > 0 ? (int)(((unsigned)tile * 37u) % (unsigned)n_ch) : 0;
+    auto chunk_of = [&](int c) { int cr = min(c, n_ch - 1) + rot; return cr >= n_ch ? cr - n_ch : cr; };
     auto load_w = [&](int p, int c) {
-        const int kc = min(c, n_ch - 1) * CH;
+        const int kc = chunk_of(c) * CH;
 #pragma unroll
         for (int i = 0; i < NI; ++i) wr[p][i] = __builtin_nontemporal_load(wsrc[i] + kc / 8);
     };
     auto load_x = [&](int p, int c) {
-        const int kc = min(c, n_ch - 1) * CH;
+        const int kc = chunk_of(c) * CH;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
